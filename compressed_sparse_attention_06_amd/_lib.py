@@ -1,0 +1,186 @@
+"""ctypes binding of libcsa.so: argument marshalling only.
+
+Every function takes torch tensors that live in device memory, passes their
+data pointers, sizes and torch's current HIP stream to the C entry point of
+the same name, and raises ``CsaError`` on a non-zero status.  All arithmetic
+happens in the HIP kernels; there is no fallback path.  When the library has
+not been built, the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
+
+CSA_F32, CSA_BF16 = 0, 1
+STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape or dtype", -3: "HIP runtime error",
+          -4: "workspace too small"}
+
+_c_int, _c_i64, _c_f, _c_sz, _c_p = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+# name -> (restype, argtypes); mirrors include/csa.h
+SIGNATURES = {
+    "csa_status_string": (ctypes.c_char_p, [_c_int]),
+    "csa_version": (_c_int, []),
+    "csa_compress": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_int, _c_p, _c_int, _c_int, _c_i64, _c_int, _c_int, _c_int,
+                              _c_int, _c_f, _c_f, _c_int, _c_int, _c_int, _c_p, _c_p, _c_int, _c_i64, _c_int, _c_p]),
+    "csa_index_score": (_c_int, [_c_p, _c_p, _c_p, _c_int, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                 _c_p, _c_p]),
+    "csa_topk_workspace_size": (_c_sz, [_c_int, _c_int, _c_int]),
+    "csa_topk": (_c_int, [_c_p, _c_p, _c_int, _c_int, _c_int, _c_p, _c_p, _c_sz, _c_p]),
+    "csa_sparse_attn_workspace_size": (_c_sz, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
+    "csa_sparse_attn": (_c_int, [_c_p, _c_p, _c_int, _c_p, _c_int, _c_p, _c_int, _c_int, _c_p, _c_p, _c_int, _c_f,
+                                 _c_int, _c_f, _c_int, _c_int, _c_int, _c_int, _c_p, _c_int, _c_p, _c_sz, _c_p]),
+    "hca_attn_workspace_size": (_c_sz, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
+    "hca_attn": (_c_int, [_c_p, _c_p, _c_int, _c_int, _c_p, _c_int, _c_int, _c_p, _c_p, _c_int, _c_f, _c_int, _c_f,
+                          _c_int, _c_int, _c_int, _c_int, _c_p, _c_int, _c_p, _c_sz, _c_p]),
+}
+
+_lib = None
+
+
+class CsaError(RuntimeError):
+    pass
+
+
+def lib():
+    """The loaded libcsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise CsaError(f"{LIB_PATH} is missing: build it with `python -m compressed_sparse_attention_06_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = handle
+    return _lib
+
+
+def _check(status, what):
+    if status != 0:
+        raise CsaError(f"{what}: {STATUS.get(status, status)} ({status})")
+
+
+def _dtype(t):
+    if t.dtype == torch.bfloat16:
+        return CSA_BF16
+    if t.dtype == torch.float32:
+        return CSA_F32
+    raise CsaError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ws(size, ws, device):
+    if size == 0:
+        return ws
+    if ws is None or ws.numel() * ws.element_size() < size:
+        ws = torch.empty(size, dtype=torch.uint8, device=device)
+    return ws
+
+
+def _bytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _dense(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise CsaError("tensors passed to the C ABI must be contiguous")
+
+
+def _rows(t):
+    """Batch stride (elements) of a [B, rows, D] tensor whose rows are packed."""
+    if t.stride(2) != 1 or (t.shape[1] > 1 and t.stride(1) != t.shape[2]):
+        raise CsaError("rows of a [B, rows, D] tensor must be contiguous and packed")
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1] * t.shape[2]
+
+
+# ---------------------------------------------------------------------------
+def csa_compress(kv, gate, gamma, out, *, ratio, overlap, rope_dim, rope_base=10000.0, eps=1e-6,
+                 kv_prev=None, gate_prev=None, tok0=0, e0=0, n_entries=None, pos=None, stream=None):
+    """kv, gate: [B, T, D] (rows contiguous); out: [B, out_cap, D]; pos: [B] int32 (ring mode) or None."""
+    B, T, D = kv.shape
+    n = (out.shape[1] - e0) if n_entries is None else n_entries
+    bstride = _rows(kv)
+    for t in (gate, kv_prev, gate_prev):
+        if t is not None and (t.shape != kv.shape or _rows(t) != bstride):
+            raise CsaError("kv, gate, kv_prev and gate_prev must share one layout")
+    _dense(gamma, pos)
+    st = lib().csa_compress(_ptr(kv), _ptr(gate), _ptr(kv_prev), _ptr(gate_prev), _dtype(kv), _ptr(gamma), B, T,
+                            bstride, D, ratio, overlap, rope_dim, rope_base, eps, tok0, e0, n, _ptr(pos),
+                            _ptr(out), _dtype(out), _rows(out), out.shape[1], _stream(stream))
+    _check(st, "csa_compress")
+    return out
+
+
+def csa_index_score(q_idx, w, idx_cache, pos, scores, *, ratio, stream=None):
+    """q_idx [B,S,H_I,D_I], w [B,S,H_I] f32, idx_cache [B,Ncap,D_I], pos [B,S] i32 -> scores [B,S,Ncap] f32."""
+    B, S, H, D = q_idx.shape
+    Ncap = idx_cache.shape[1]
+    _dense(q_idx, w, idx_cache, pos, scores)
+    st = lib().csa_index_score(_ptr(q_idx), _ptr(w), _ptr(idx_cache), _dtype(q_idx), _ptr(pos), B, S, H, D, Ncap,
+                               ratio, _ptr(scores), _stream(stream))
+    _check(st, "csa_index_score")
+    return scores
+
+
+def csa_topk_workspace_size(R, N, k):
+    return int(lib().csa_topk_workspace_size(R, N, k))
+
+
+def csa_topk(scores, n_valid, k, idx, *, ws=None, stream=None):
+    """scores [R,N] f32, n_valid [R] i32 or None -> idx [R,k] i32 (ascending, -1 padded)."""
+    R, N = scores.shape
+    _dense(scores, n_valid, idx)
+    ws = _ws(csa_topk_workspace_size(R, N, k), ws, scores.device)
+    st = lib().csa_topk(_ptr(scores), _ptr(n_valid), R, N, k, _ptr(idx), _ptr(ws), _bytes(ws), _stream(stream))
+    _check(st, "csa_topk")
+    return idx
+
+
+def csa_sparse_attn_workspace_size(B, S, H, D, k, window):
+    return int(lib().csa_sparse_attn_workspace_size(B, S, H, D, k, window))
+
+
+def csa_sparse_attn(q, cmp, idx, win, pos, sink, out, *, window, scale, rope_dim, rope_base=10000.0,
+                    ws=None, stream=None):
+    """q [B,S,H,D], cmp [B,Ncap,D], idx [B,S,k] i32, win [B,Wcap,D], pos [B,S] i32, sink [H] f32 -> out."""
+    B, S, H, D = q.shape
+    k = idx.shape[-1]
+    _dense(q, cmp, idx, win, pos, sink, out)
+    ws = _ws(csa_sparse_attn_workspace_size(B, S, H, D, k, window), ws, q.device)
+    st = lib().csa_sparse_attn(_ptr(q), _ptr(cmp), cmp.shape[1], _ptr(idx), k, _ptr(win), win.shape[1], window,
+                               _ptr(pos), _ptr(sink), _dtype(q), scale, rope_dim, rope_base, B, S, H, D, _ptr(out),
+                               _dtype(out), _ptr(ws), _bytes(ws), _stream(stream))
+    _check(st, "csa_sparse_attn")
+    return out
+
+
+def hca_attn_workspace_size(B, S, H, D, Ncap, window):
+    return int(lib().hca_attn_workspace_size(B, S, H, D, Ncap, window))
+
+
+def hca_attn(q, cmp, win, pos, sink, out, *, ratio, window, scale, rope_dim, rope_base=10000.0,
+             ws=None, stream=None):
+    """q [B,S,H,D], cmp [B,Ncap,D], win [B,Wcap,D], pos [B,S] i32, sink [H] f32 -> out [B,S,H,D]."""
+    B, S, H, D = q.shape
+    Ncap = cmp.shape[1]
+    _dense(q, cmp, win, pos, sink, out)
+    ws = _ws(hca_attn_workspace_size(B, S, H, D, Ncap, window), ws, q.device)
+    st = lib().hca_attn(_ptr(q), _ptr(cmp), Ncap, ratio, _ptr(win), win.shape[1], window, _ptr(pos), _ptr(sink),
+                        _dtype(q), scale, rope_dim, rope_base, B, S, H, D, _ptr(out), _dtype(out), _ptr(ws),
+                        _bytes(ws), _stream(stream))
+    _check(st, "hca_attn")
+    return out

@@ -1,0 +1,83 @@
+// Device helpers shared by the gfx950 kernels: bf16 storage, matrix-core
+// operand types, wave reductions and the RoPE angle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "csa.h"
+
+namespace csa {
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16;
+
+// ---------------------------------------------------------------------------
+// bfloat16 storage (raw 16-bit patterns in memory)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// float -> bf16 bits, round to nearest even (inputs are finite)
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Element i of a tensor of either dtype, as float.
+__device__ __forceinline__ float load_elem(const void* p, int dtype, int64_t i) {
+  if (dtype == CSA_BF16) return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+  return static_cast<const float*>(p)[i];
+}
+__device__ __forceinline__ void store_elem(void* p, int dtype, int64_t i, float v) {
+  if (dtype == CSA_BF16)
+    static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(f32_to_bf16_bits(v));
+  else
+    static_cast<float*>(p)[i] = v;
+}
+
+// 8 consecutive bf16 (16 bytes) as a matrix-core operand.
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
+  bf16x8 r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Wave reductions (64 lanes)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// RoPE angle of pair i at position p: p * base^(-2i/rope_dim), formed and
+// range-reduced in double so that positions near 2^20 keep full accuracy.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void rope_cos_sin(int64_t p, int i, int rope_dim, float base,
+                                             float* c, float* s) {
+  double theta = exp2(-2.0 * double(i) / double(rope_dim) * log2(double(base)));
+  double sn, cs;
+  sincos(double(p) * theta, &sn, &cs);
+  *c = float(cs);
+  *s = float(sn);
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace csa

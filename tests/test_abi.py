@@ -1,0 +1,133 @@
+"""The C ABI library (no GPU): it builds and loads, exports every symbol that
+include/csa.h declares, and rejects invalid arguments on the host before any
+HIP call.  No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+
+INVALID, UNSUPPORTED, WORKSPACE = -1, -2, -4
+P = ctypes.c_void_p(0x10000)  # a non-null address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:csa|hca)_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import compressed_sparse_attention_06_amd as pkg
+    if not os.path.exists(pkg.LIB_PATH):
+        from compressed_sparse_attention_06_amd import build
+        build.build()
+    return pkg.lib()
+
+
+def test_header_declares_the_five_entry_points():
+    names = declared_functions()
+    for n in ("csa_compress", "csa_index_score", "csa_topk", "csa_sparse_attn", "hca_attn"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from compressed_sparse_attention_06_amd._lib import SIGNATURES
+    names = declared_functions()
+    assert set(names) == set(SIGNATURES), "binding table and header disagree"
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version(lib):
+    assert lib.csa_status_string(0) == b"ok"
+    assert lib.csa_status_string(-1) == b"invalid argument"
+    assert lib.csa_status_string(-4) == b"workspace too small"
+    assert lib.csa_status_string(7) == b"unknown status"
+    assert lib.csa_version() >= 10000
+
+
+def _compress(lib, **kw):
+    a = dict(kv=P, gate=P, kv_prev=None, gate_prev=None, in_dtype=1, gamma=P, B=1, T=16, in_bstride=16 * 512,
+             D=512, ratio=4, overlap=1, rope_dim=64, rope_base=10000.0, eps=1e-6, tok0=0, e0=0, n_entries=4,
+             pos=None, out=P, out_dtype=0, out_bstride=4 * 512, out_cap=4, stream=None)
+    a.update(kw)
+    return lib.csa_compress(*a.values())
+
+
+@pytest.mark.parametrize("bad", [
+    dict(kv=None), dict(gate=None), dict(gamma=None), dict(out=None), dict(in_dtype=2), dict(out_dtype=-1),
+    dict(ratio=0), dict(overlap=2), dict(rope_dim=63), dict(rope_dim=514), dict(eps=-1.0), dict(rope_base=0.0),
+    dict(T=0), dict(B=-1), dict(in_bstride=100), dict(out_cap=3), dict(n_entries=5),
+    dict(tok0=1),                                  # entry 0 needs token 0
+    dict(e0=1, n_entries=3, tok0=1, T=15),         # entry 1 with overlap needs token 0
+    dict(pos=P, T=7),                              # ring smaller than (1+overlap)*ratio
+])
+def test_compress_rejects(lib, bad):
+    assert _compress(lib, **bad) == INVALID
+
+
+def test_compress_rejects_huge_rows(lib):
+    assert _compress(lib, D=8200, rope_dim=64, in_bstride=16 * 8200, out_bstride=4 * 8200) == UNSUPPORTED
+
+
+def _index(lib, **kw):
+    a = dict(q=P, w=P, cache=P, dtype=1, pos=P, B=2, S=1, H=64, D=128, Ncap=1000, ratio=4, scores=P, stream=None)
+    a.update(kw)
+    return lib.csa_index_score(*a.values())
+
+
+@pytest.mark.parametrize("bad", [dict(q=None), dict(w=None), dict(cache=None), dict(pos=None), dict(scores=None),
+                                 dict(dtype=3), dict(H=0), dict(D=0), dict(Ncap=-1), dict(ratio=0), dict(B=-2)])
+def test_index_score_rejects(lib, bad):
+    assert _index(lib, **bad) == INVALID
+
+
+def test_index_score_unsupported(lib):
+    assert _index(lib, dtype=0, H=200, D=128) == UNSUPPORTED        # vector path limit
+    assert _index(lib, Ncap=65535 * 256 + 1) == UNSUPPORTED
+
+
+def test_topk_validation_and_workspace(lib):
+    assert lib.csa_topk(None, None, 1, 10, 4, P, None, 0, None) == INVALID
+    assert lib.csa_topk(P, None, 1, 10, 0, P, None, 0, None) == INVALID
+    assert lib.csa_topk(P, None, 1, 10, 4097, P, None, 0, None) == INVALID
+    assert lib.csa_topk_workspace_size(8, 16384, 512) == 0
+    need = lib.csa_topk_workspace_size(32, 262144, 512)
+    assert need == 2 * 32 * 16 * 512 * 8
+    assert lib.csa_topk(P, None, 32, 262144, 512, P, P, need - 1, None) == WORKSPACE
+    assert lib.csa_topk(P, None, 32, 262144, 512, P, None, need, None) == WORKSPACE
+
+
+def _attn(lib, **kw):
+    a = dict(q=P, cmp=P, Ncap=1000, idx=P, k=512, win=P, Wcap=128, window=128, pos=P, sink=P, dtype=1, scale=0.04,
+             rope_dim=64, rope_base=10000.0, B=8, S=1, H=64, D=512, out=P, out_dtype=0, ws=P, ws_bytes=1 << 40,
+             stream=None)
+    a.update(kw)
+    return lib.csa_sparse_attn(*a.values())
+
+
+@pytest.mark.parametrize("bad", [dict(q=None), dict(cmp=None), dict(idx=None), dict(pos=None), dict(sink=None),
+                                 dict(out=None), dict(win=None), dict(Wcap=64), dict(window=-1), dict(k=-1),
+                                 dict(rope_dim=65), dict(rope_dim=600), dict(dtype=5), dict(H=0),
+                                 dict(scale=float("inf"))])
+def test_sparse_attn_rejects(lib, bad):
+    assert _attn(lib, **bad) == INVALID
+
+
+def test_attn_workspace_sizes(lib):
+    ws = lib.csa_sparse_attn_workspace_size(8, 1, 64, 512, 512, 128)
+    assert ws > 0 and ws % (64 * 514 * 4 * 8) == 0       # whole (query, split, head) partials
+    assert lib.csa_sparse_attn_workspace_size(1, 8192, 64, 512, 512, 128) == 0  # one split per query
+    assert _attn(lib, ws=None, ws_bytes=0) == WORKSPACE
+    assert _attn(lib, ws_bytes=ws - 1) == WORKSPACE
+    assert _attn(lib, dtype=0, D=2048, H=64, rope_dim=64) == UNSUPPORTED
+    hws = lib.hca_attn_workspace_size(4, 1, 64, 512, 8192, 128)
+    assert hws > 0
+    assert lib.hca_attn(P, P, 8192, 0, P, 128, 128, P, P, 1, 0.04, 64, 1e4, 4, 1, 64, 512, P, 0, P, hws, None) == INVALID
+    assert lib.hca_attn(P, P, 8192, 128, P, 128, 128, P, P, 1, 0.04, 64, 1e4, 4, 1, 64, 512, P, 0, P, hws - 1,
+                        None) == WORKSPACE

@@ -1,0 +1,318 @@
+"""GPU parity of each C-ABI entry point against the float64 oracle on the same
+seeded inputs (sizes span several tiles plus a ragged tail)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_util import (assert_attn, assert_bf16_matches, assert_normwise, dev, dev_bf16, host, progress,
+                            topk_set_check)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import compressed_sparse_attention_06_amd as csa
+    csa.lib()
+    return csa
+
+
+@pytest.fixture(autouse=True)
+def _name(request):
+    progress(request.node.nodeid)
+    yield
+    torch.cuda.synchronize()
+
+
+def csa_mod():
+    import compressed_sparse_attention_06_amd as csa
+    return csa
+
+
+def rows_bf16(seed, shape, unit=False):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(shape)
+    if unit:
+        x /= np.sqrt(np.mean(x * x, axis=-1, keepdims=True))
+    return synth.bf16_bits(x.astype(np.float32))
+
+
+# ---------------------------------------------------------------------------
+# Compressor
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("D,ratio,overlap,rope,T,tok0,e0,n", [
+    (512, 4, 1, 64, 40, 0, 0, 10),       # CSA KV role, from entry 0
+    (512, 4, 1, 64, 24, 8, 3, 5),        # ragged span inside a longer sequence
+    (128, 4, 1, 64, 36, 0, 0, 9),        # index-key role
+    (512, 128, 0, 64, 384, 0, 0, 3),     # HCA ratio, no overlap
+    (256, 2, 1, 32, 14, 0, 0, 7),        # other lane width
+    (96, 4, 1, 16, 20, 0, 0, 5),         # general path (D not a lane multiple)
+])
+def test_compress_span(D, ratio, overlap, rope, T, tok0, e0, n):
+    csa = csa_mod()
+    B = 2
+    kv = rows_bf16(1, (B, T, D))
+    gate = rows_bf16(2, (B, T, D))
+    gamma = (1 + 0.1 * np.random.default_rng(3).standard_normal(D)).astype(np.float32)
+    cap = e0 + n + 2
+    out32 = torch.full((B, cap, D), 7.0, device="cuda")
+    out16 = torch.zeros((B, cap, D), device="cuda", dtype=torch.bfloat16)
+    for out in (out32, out16):
+        csa.csa_compress(dev_bf16(kv), dev_bf16(gate), dev(gamma), out, ratio=ratio, overlap=overlap,
+                         rope_dim=rope, tok0=tok0, e0=e0, n_entries=n)
+    torch.cuda.synchronize()
+    g32, g16 = host(out32), host(out16)
+    for b in range(B):
+        # oracle over a full-length view: token rows placed at their absolute index
+        full_kv = np.zeros((tok0 + T, D)); full_kv[tok0:] = synth.bf16_to_f64(kv[b])
+        full_g = np.zeros((tok0 + T, D)); full_g[tok0:] = synth.bf16_to_f64(gate[b])
+        want = np.stack([oracle.compress_entry(e, full_kv, full_g, full_kv, full_g, gamma, ratio, overlap, rope,
+                                               10000.0, 1e-6) for e in range(e0, e0 + n)])
+        assert_normwise(g32[b, e0:e0 + n], want, what=f"fp32 b={b}")
+        assert_bf16_matches(g16[b, e0:e0 + n], want, what=f"bf16 b={b}")
+        assert np.all(g32[b, :e0] == 7.0) and np.all(g32[b, e0 + n:] == 7.0)
+
+
+def test_compress_ring_mode_matches_span_mode_bitwise():
+    """Decode-time append (ring of the last 2r tokens, per-sequence position)
+    builds the same entries as the prefill span mode, bit for bit."""
+    csa = csa_mod()
+    D, r, B, T = 512, 4, 4, 48
+    kv = rows_bf16(11, (B, T, D))
+    gate = rows_bf16(12, (B, T, D))
+    gamma = dev(np.ones(D, np.float32))
+    cap = T // r
+    span = torch.zeros((B, cap, D), device="cuda")
+    csa.csa_compress(dev_bf16(kv), dev_bf16(gate), gamma, span, ratio=r, overlap=1, rope_dim=64)
+    ring_out = torch.full((B, cap, D), 5.0, device="cuda")
+    pos = np.array([3, 22, 47, 45], np.int32)  # emits, no, emits, no
+    ring = np.zeros((B, 2 * r, D), np.uint16)
+    ring_g = np.zeros((B, 2 * r, D), np.uint16)
+    for b in range(B):
+        for t in range(max(0, pos[b] - 2 * r + 1), pos[b] + 1):
+            ring[b, t % (2 * r)] = kv[b, t]
+            ring_g[b, t % (2 * r)] = gate[b, t]
+    csa.csa_compress(dev_bf16(ring), dev_bf16(ring_g), gamma, ring_out, ratio=r, overlap=1, rope_dim=64,
+                     pos=dev(pos))
+    torch.cuda.synchronize()
+    s, g = span.cpu().numpy(), ring_out.cpu().numpy()
+    for b in range(B):
+        if (pos[b] + 1) % r == 0:
+            e = pos[b] // r
+            assert np.array_equal(g[b, e], s[b, e])
+            g[b, e] = 5.0
+        assert np.all(g[b] == 5.0)
+
+
+# ---------------------------------------------------------------------------
+# Indexer
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("H,D,dtype", [(64, 128, "bf16"), (2, 16, "f32"), (4, 32, "bf16")])
+def test_index_score(H, D, dtype):
+    csa = csa_mod()
+    B, S, Ncap, r = 2, 3, 1000, 4
+    pos = np.array([[3999, 2000, 0], [-1, 4003, 1023]], np.int32)
+    q = rows_bf16(21, (B, S, H, D), unit=True)
+    k = rows_bf16(22, (B, Ncap, D), unit=True)
+    w = (np.random.default_rng(23).standard_normal((B, S, H)) / math.sqrt(D) / math.sqrt(H)).astype(np.float32)
+    if dtype == "bf16":
+        qd, kd = dev_bf16(q), dev_bf16(k)
+    else:
+        qd, kd = dev(synth.bf16_to_f32(q)), dev(synth.bf16_to_f32(k))
+    scores = torch.empty((B, S, Ncap), device="cuda")
+    csa.csa_index_score(qd, dev(w), kd, dev(pos), scores, ratio=r)
+    got = scores.cpu().numpy()
+    for b in range(B):
+        want = np.stack([oracle.index_score(synth.bf16_to_f64(q[b, s]), w[b, s], synth.bf16_to_f64(k[b]),
+                                            oracle.visible(int(pos[b, s]), r)) for s in range(S)])
+        assert_normwise(got[b], want, what=f"b={b}")
+
+
+# ---------------------------------------------------------------------------
+# Top-k (identical float32 scores on both sides: bit-exact sets)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("R,N,k,nvalid", [
+    (3, 100, 4, None), (5, 2048, 512, "ragged"), (4, 5000, 512, None), (2, 16384, 512, None),
+    (3, 40000, 512, "ragged"), (2, 300000, 1024, None), (2, 700, 512, None), (64, 2048, 512, "causal"),
+])
+def test_topk_exact(R, N, k, nvalid):
+    csa = csa_mod()
+    s = synth.topk_scores(7, R, N, tie_frac=0.2, b=N)
+    if nvalid == "ragged":
+        nv = np.random.default_rng(N).integers(0, N + 1, size=R).astype(np.int32)
+        nv[0] = N
+    elif nvalid == "causal":
+        nv = ((np.arange(R) * 97 + 1) // 4 % (N + 1)).astype(np.int32)
+    else:
+        nv = None
+    s[:, N // 3] = -np.inf  # invisible entries are never picked
+    idx = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    csa.csa_topk(dev(s), None if nv is None else dev(nv), k, idx)
+    got = idx.cpu().numpy()
+    for r in range(R):
+        want = oracle.topk(s[r].astype(np.float64), N if nv is None else int(nv[r]), k)
+        assert np.array_equal(got[r], want), f"row {r}"
+
+
+# ---------------------------------------------------------------------------
+# Attention
+# ---------------------------------------------------------------------------
+def _attn_case(B, S, Ncap, k, window, Wcap, pos, seed, H=64, D=512, rope=64):
+    q = rows_bf16(seed, (B, S, H, D), unit=True)
+    cmp = rows_bf16(seed + 1, (B, Ncap, D), unit=True)
+    win = rows_bf16(seed + 2, (B, Wcap, D), unit=True)
+    sink = np.random.default_rng(seed + 3).standard_normal(H).astype(np.float32)
+    sel = np.full((B, S, k), -1, np.int32)
+    for b in range(B):
+        for s in range(S):
+            nv = min(oracle.visible(int(pos[b, s]), 4), Ncap)
+            sel[b, s] = synth.random_selection(seed, nv, k, b=b, t=s)
+    sel[0, 0, :3] = [Ncap + 5, -7, sel[0, 0, 3]]  # out-of-range entries are skipped
+    return q, cmp, win, sink, sel
+
+
+def _oracle_attn(q, cmp, win, sink, sel, pos, window, Wcap, scale, rope, hca_ratio=None):
+    B, S = pos.shape
+    out = np.zeros(q.shape)
+    for b in range(B):
+        cmpb = synth.bf16_to_f64(cmp[b])
+        for s in range(S):
+            p = int(pos[b, s])
+            wr = [synth.bf16_to_f64(win[b, pp % Wcap]) for pp in oracle.window_positions(p, window)] if p >= 0 else []
+            wr = np.stack(wr) if wr else np.zeros((0, cmp.shape[-1]))
+            qq = synth.bf16_to_f64(q[b, s])
+            if hca_ratio is None:
+                sl = sel[b, s]
+                sl = np.where((sl >= 0) & (sl < cmp.shape[1]), sl, -1)
+                out[b, s] = oracle.sparse_attn(qq, cmpb, sl, wr, sink, scale, p, rope)
+            else:
+                nv = min(oracle.visible(p, hca_ratio), cmp.shape[1]) if p >= 0 else 0
+                out[b, s] = oracle.hca_attn(qq, cmpb, nv, wr, sink, scale, p, rope)
+    return out
+
+
+@pytest.mark.parametrize("B,S,pos_kind", [(2, 2, "decode"), (1, 600, "prefill")])
+def test_sparse_attn_mfma(B, S, pos_kind):
+    csa = csa_mod()
+    Ncap, k, window, D = 2048, 512, 128, 512
+    if pos_kind == "decode":
+        pos = np.array([[8191, 50], [1048575, 0]], np.int32)
+        Wcap = 128
+    else:
+        pos = (np.arange(S, dtype=np.int32) + 7000)[None]
+        Wcap = 8192
+    q, cmp, win, sink, sel = _attn_case(B, S, Ncap, k, window, Wcap, pos, 31)
+    scale = 1 / math.sqrt(D)
+    want = _oracle_attn(q, cmp, win, sink, sel, pos, window, Wcap, scale, 64)
+    for odt in (torch.float32, torch.bfloat16):
+        out = torch.empty((B, S, 64, D), device="cuda", dtype=odt)
+        csa.csa_sparse_attn(dev_bf16(q), dev_bf16(cmp), dev(sel), dev_bf16(win), dev(pos), dev(sink), out,
+                            window=window, scale=scale, rope_dim=64)
+        got = host(out)
+        assert_attn(got, want, what=f"{pos_kind} {odt}")
+
+
+def test_hca_attn_mfma():
+    csa = csa_mod()
+    B, S, Ncap, window, Wcap, D, r = 3, 1, 300, 128, 128, 512, 128
+    pos = np.array([[300 * 128 + 5], [100 * 128 - 1], [77]], np.int32)
+    q, cmp, win, sink, _ = _attn_case(B, S, Ncap, 4, window, Wcap, pos, 41)
+    scale = 1 / math.sqrt(D)
+    want = _oracle_attn(q, cmp, win, sink, None, pos, window, Wcap, scale, 64, hca_ratio=r)
+    out = torch.empty((B, S, 64, D), device="cuda")
+    csa.hca_attn(dev_bf16(q), dev_bf16(cmp), dev_bf16(win), dev(pos), dev(sink), out, ratio=r, window=window,
+                 scale=scale, rope_dim=64)
+    assert_attn(host(out), want, what="hca")
+
+
+def test_attn_vector_path_fp32():
+    csa = csa_mod()
+    B, S, H, D, Ncap, k, window, Wcap = 1, 5, 3, 48, 40, 6, 4, 64
+    pos = np.array([[0, 3, 17, 40, 63]], np.int32)
+    q, cmp, win, sink, sel = _attn_case(B, S, Ncap, k, window, Wcap, pos, 51, H=H, D=D, rope=16)
+    f32 = lambda x: dev(synth.bf16_to_f32(x))
+    scale = 0.3
+    want = _oracle_attn(q, cmp, win, sink, sel, pos, window, Wcap, scale, 16)
+    out = torch.empty((B, S, H, D), device="cuda")
+    csa.csa_sparse_attn(f32(q), f32(cmp), dev(sel), f32(win), dev(pos), dev(sink), out, window=window, scale=scale,
+                        rope_dim=16)
+    assert_attn(host(out), want, what="csa vector", max_abs=1e-4, mean_abs=1e-5)
+    want = _oracle_attn(q, cmp, win, sink, None, pos, window, Wcap, scale, 16, hca_ratio=4)
+    csa.hca_attn(f32(q), f32(cmp), f32(win), dev(pos), dev(sink), out, ratio=4, window=window, scale=scale,
+                 rope_dim=16)
+    assert_attn(host(out), want, what="hca vector", max_abs=1e-4, mean_abs=1e-5)
+
+
+# ---------------------------------------------------------------------------
+# Tiny configuration end to end: prefill 16, then 4 streamed decode tokens
+# ---------------------------------------------------------------------------
+def test_tiny_config_end_to_end():
+    csa = csa_mod()
+    cfg = synth.TINY
+    inp = synth.tiny_inputs(cfg)
+    T0, T = cfg.T_prefill, cfg.T_prefill + cfg.T_decode
+    want = oracle.pipeline.tiny_prefill(inp, cfg, T)
+    D, DI, H, HI, r, k, W = cfg.D, cfg.D_I, cfg.H, cfg.H_I, cfg.ratio, cfg.k, cfg.window
+    cap = T // r
+    g = lambda name: dev(inp[name])
+    kv_cache = torch.zeros((1, cap, D), device="cuda")
+    idx_cache = torch.zeros((1, cap, DI), device="cuda")
+    win = torch.zeros((1, T, D), device="cuda")
+    zeros_g = torch.zeros((1, T, D), device="cuda")
+    scale = 1 / math.sqrt(D)
+    outs, sels = [], []
+    # prefill of the first T0 tokens
+    kv, gate = g("kv")[None, :T0], g("gate")[None, :T0]
+    csa.csa_compress(kv, gate, g("gamma"), kv_cache, ratio=r, overlap=1, rope_dim=cfg.rope_dim, n_entries=T0 // r)
+    csa.csa_compress(g("k_idx")[None, :T0], g("g_idx")[None, :T0], g("gamma_idx"), idx_cache, ratio=r, overlap=1,
+                     rope_dim=cfg.rope_dim_idx, n_entries=T0 // r)
+    csa.csa_compress(kv, zeros_g[:, :T0], g("gamma_win"), win, ratio=1, overlap=0, rope_dim=cfg.rope_dim,
+                     n_entries=T0)
+    pos = dev(np.arange(T0, dtype=np.int32)[None])
+    scores = torch.empty((1, T0, cap), device="cuda")
+    csa.csa_index_score(g("q_idx")[None, :T0], g("w")[None, :T0], idx_cache, pos, scores, ratio=r)
+    sel = torch.empty((T0, k), dtype=torch.int32, device="cuda")
+    csa.csa_topk(scores.view(T0, cap), None, k, sel)
+    out = torch.empty((1, T0, H, D), device="cuda")
+    csa.csa_sparse_attn(g("q")[None, :T0], kv_cache, sel.view(1, T0, k), win, pos, g("sink"), out, window=W,
+                        scale=scale, rope_dim=cfg.rope_dim)
+    outs += list(host(out)[0])
+    sels += list(sel.cpu().numpy())
+    got_scores = list(scores.cpu().numpy()[0])
+    # streamed decode tokens
+    R = 2 * r
+    for t in range(T0, T):
+        ring = lambda name, d: dev(np.stack([inp[name][tt] if tt >= 0 else np.zeros(d, np.float32)
+                                             for tt in [t - ((t - j) % R) for j in range(R)]])[None])
+        p1 = dev(np.array([t], np.int32))
+        csa.csa_compress(ring("kv", D), ring("gate", D), g("gamma"), kv_cache, ratio=r, overlap=1,
+                         rope_dim=cfg.rope_dim, pos=p1)
+        csa.csa_compress(ring("k_idx", DI), ring("g_idx", DI), g("gamma_idx"), idx_cache, ratio=r, overlap=1,
+                         rope_dim=cfg.rope_dim_idx, pos=p1)
+        csa.csa_compress(g("kv")[None, t:t + 1], zeros_g[:, :1], g("gamma_win"), win, ratio=1, overlap=0,
+                         rope_dim=cfg.rope_dim, tok0=t, e0=t, n_entries=1)
+        sc = torch.empty((1, 1, cap), device="cuda")
+        csa.csa_index_score(g("q_idx")[None, t:t + 1], g("w")[None, t:t + 1], idx_cache, p1.view(1, 1), sc, ratio=r)
+        s1 = torch.empty((1, k), dtype=torch.int32, device="cuda")
+        csa.csa_topk(sc.view(1, cap), None, k, s1)
+        o1 = torch.empty((1, 1, H, D), device="cuda")
+        csa.csa_sparse_attn(g("q")[None, t:t + 1], kv_cache, s1.view(1, 1, k), win, p1.view(1, 1), g("sink"), o1,
+                            window=W, scale=scale, rope_dim=cfg.rope_dim)
+        outs.append(host(o1)[0, 0])
+        sels.append(s1.cpu().numpy()[0])
+        got_scores.append(sc.cpu().numpy()[0, 0])
+    assert_normwise(host(kv_cache)[0], want["kv_cache"], what="kv cache")
+    assert_normwise(host(idx_cache)[0], want["idx_cache"], what="index cache")
+    assert_normwise(host(win)[0], want["win"], what="window rows")
+    for t in range(T):
+        assert_normwise(got_scores[t][None], want["scores"][t][None], what=f"scores t={t}")
+    topk_set_check(np.stack(sels), np.stack(want["scores"]), np.stack(want["sel"]), k)
+    for t in range(T):
+        if set(sels[t]) == set(want["sel"][t]):
+            assert_attn(outs[t], want["out"][t], what=f"out t={t}", max_abs=1e-4, mean_abs=1e-5)
