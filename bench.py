@@ -1,0 +1,544 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA / HCA compressed-KV attention path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload csa_decode_64k] [--extra ...]
+
+A step is one pass of the whole path over one batch of synthetic inputs that
+are already resident in HBM:
+  decode (CSA):  append the completed group to both compressed caches (KV and
+                 index keys), score every visible entry, top-k, sparse attention
+  decode (HCA):  append to the compressed KV cache, attention over all entries
+  prefill (CSA): compress every group of both roles, score, top-k, attention
+Each step reads its caches from one of 16 copies in rotation, so the 256 MiB
+Infinity Cache cannot serve the stream.  Steps are replayed from HIP graphs
+(one graph per copy).  Per-kernel durations are measured with HIP events in an
+eager pass queued behind a GPU spin (so launches run back to back).
+
+Prints ONE JSON line (rank 0).  The CPU baseline is the float64 oracle run on
+a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "decode query-tokens/s + achieved HBM GB/s at 64K/1M ctx; prefill indexer MFMA util"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, TFLOP/s
+COPIES = 16
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="csa_decode_64k", choices=sorted(synth.CONFIGS))
+    ap.add_argument("--extra", default="hca_decode_1m,csa_prefill_8k",
+                    help="comma-separated secondary workloads measured after the main one ('' for none)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-only", default="", help="profiling aid: replay only this kernel's graphs")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# Device workloads
+# ---------------------------------------------------------------------------
+def _bf16(bits, device):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def _f32(x, device):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+
+
+class DecodeWorkload:
+    """One decode step for B sequences (CSA or HCA) on rotated cache copies."""
+
+    def __init__(self, cfg, device, copies=COPIES):
+        import torch
+        self.cfg, self.device = cfg, device
+        B, D, DI = cfg.B, cfg.D, cfg.D_I
+        self.lengths = synth.decode_lengths(cfg)
+        self.Ncap = synth.decode_capacity(cfg)
+        self.R = synth.staging_rows(cfg)
+        self.seqs = [synth.decode_seq(cfg, b, self.lengths) for b in range(B)]
+        shared = synth.decode_shared(cfg)
+        self.pos_np = np.array([s.pos for s in self.seqs], np.int32)
+        self.n_vis = np.array([s.n_vis for s in self.seqs], np.int64)
+        self.pos = torch.from_numpy(self.pos_np).to(device)
+        self.pos2 = self.pos.view(B, 1)
+        self.sink = _f32(shared["sink"], device)
+        self.gamma = _f32(shared["gamma"], device)
+        self.gamma_idx = _f32(shared["gamma_idx"], device)
+        self.q = _bf16(np.stack([s.q for s in self.seqs])[:, None], device)
+        self.win = _bf16(np.stack([s.win for s in self.seqs]), device)
+        self.kv_stage = _bf16(np.stack([s.kv_stage for s in self.seqs]), device)
+        self.gate_stage = _bf16(np.stack([s.gate_stage for s in self.seqs]), device)
+        # caches: the first copy from the seeded generator, the others device copies
+        self.copies = copies if cfg.ctx_lo == 0 else 1
+        kv0 = torch.empty((B, self.Ncap, D), dtype=torch.bfloat16, device=device)
+        for b in range(B):
+            kv0[b] = _bf16(synth.kv_cache_rows(cfg, b, self.Ncap), device)
+        self.kv = [kv0] + [kv0.clone() for _ in range(self.copies - 1)]
+        self.out = torch.empty((B, 1, cfg.H, D), dtype=torch.float32, device=device)
+        if cfg.csa:
+            self.q_idx = _bf16(np.stack([s.q_idx for s in self.seqs])[:, None], device)
+            self.w = _f32(np.stack([s.w for s in self.seqs])[:, None], device)
+            self.ki_stage = _bf16(np.stack([s.ki_stage for s in self.seqs]), device)
+            self.gi_stage = _bf16(np.stack([s.gi_stage for s in self.seqs]), device)
+            ic0 = torch.empty((B, self.Ncap, DI), dtype=torch.bfloat16, device=device)
+            for b in range(B):
+                ic0[b] = _bf16(synth.idx_cache_rows(cfg, b, self.Ncap), device)
+            self.idx_cache = [ic0] + [ic0.clone() for _ in range(self.copies - 1)]
+            self.scores = torch.empty((B, 1, self.Ncap), dtype=torch.float32, device=device)
+            self.sel = torch.empty((B, 1, cfg.k), dtype=torch.int32, device=device)
+            import compressed_sparse_attention_06_amd as csa
+            self.ws_topk = torch.empty(max(1, csa.csa_topk_workspace_size(B, self.Ncap, cfg.k)), dtype=torch.uint8,
+                                       device=device)
+            self.ws_attn = torch.empty(max(1, csa.csa_sparse_attn_workspace_size(B, 1, cfg.H, D, cfg.k, cfg.window)),
+                                       dtype=torch.uint8, device=device)
+        else:
+            import compressed_sparse_attention_06_amd as csa
+            self.ws_attn = torch.empty(max(1, csa.hca_attn_workspace_size(B, 1, cfg.H, D, self.Ncap, cfg.window)),
+                                       dtype=torch.uint8, device=device)
+        torch.cuda.synchronize()
+
+    # the kernels of one step, as (name, callable) in launch order
+    def launches(self, c):
+        import compressed_sparse_attention_06_amd as csa
+        cfg = self.cfg
+        c = c % self.copies
+        scale = 1.0 / math.sqrt(cfg.D)
+        L = [("compress_kv", lambda: csa.csa_compress(
+            self.kv_stage, self.gate_stage, self.gamma, self.kv[c], ratio=cfg.ratio, overlap=cfg.overlap,
+            rope_dim=cfg.rope_dim, rope_base=cfg.rope_base, eps=cfg.eps, pos=self.pos))]
+        if cfg.csa:
+            L += [
+                ("compress_idx", lambda: csa.csa_compress(
+                    self.ki_stage, self.gi_stage, self.gamma_idx, self.idx_cache[c], ratio=cfg.ratio,
+                    overlap=cfg.overlap, rope_dim=cfg.rope_dim_idx, rope_base=cfg.rope_base, eps=cfg.eps,
+                    pos=self.pos)),
+                ("index_score", lambda: csa.csa_index_score(self.q_idx, self.w, self.idx_cache[c], self.pos2,
+                                                            self.scores, ratio=cfg.ratio)),
+                ("topk", lambda: csa.csa_topk(self.scores.view(cfg.B, self.Ncap), None, cfg.k,
+                                              self.sel.view(cfg.B, cfg.k), ws=self.ws_topk)),
+                ("sparse_attn", lambda: csa.csa_sparse_attn(
+                    self.q, self.kv[c], self.sel, self.win, self.pos2, self.sink, self.out, window=cfg.window,
+                    scale=scale, rope_dim=cfg.rope_dim, rope_base=cfg.rope_base, ws=self.ws_attn)),
+            ]
+        else:
+            L += [("hca_attn", lambda: csa.hca_attn(
+                self.q, self.kv[c], self.win, self.pos2, self.sink, self.out, ratio=cfg.ratio, window=cfg.window,
+                scale=scale, rope_dim=cfg.rope_dim, rope_base=cfg.rope_base, ws=self.ws_attn))]
+        return L
+
+    def queries(self):
+        return self.cfg.B
+
+    def dominant(self):
+        return "index_score" if self.cfg.csa else "hca_attn"
+
+    def algorithmic(self):
+        """Algorithmic HBM bytes of each kernel of one step (and flops)."""
+        cfg, B = self.cfg, self.cfg.B
+        D, DI, H, HI = cfg.D, cfg.D_I, cfg.H, cfg.H_I
+        emit = int(np.sum((self.pos_np + 1) % cfg.ratio == 0))
+        rows_in = (1 + cfg.overlap) * cfg.ratio
+        vis = self.n_vis
+        win = np.minimum(cfg.window, self.pos_np + 1)
+        by = {"compress_kv": emit * (2 * rows_in * D * 2 + D * 2) + D * 4}
+        fl = {}
+        if cfg.csa:
+            by["compress_idx"] = emit * (2 * rows_in * DI * 2 + DI * 2) + DI * 4
+            by["index_score"] = int(np.sum(vis * DI * 2) + B * (HI * DI * 2 + HI * 4) + B * self.Ncap * 4)
+            fl["index_score"] = int(np.sum(vis) * HI * DI * 2)
+            by["topk"] = int(B * self.Ncap * 4 + B * cfg.k * 4)
+            sel = np.minimum(vis, cfg.k)
+            by["sparse_attn"] = int(np.sum((sel + win) * D * 2) + B * (H * D * 2 + cfg.k * 4 + H * D * 4))
+            fl["sparse_attn"] = int(np.sum(sel + win) * H * D * 4)
+        else:
+            by["hca_attn"] = int(np.sum((vis + win) * D * 2) + B * (H * D * 2 + H * D * 4))
+            fl["hca_attn"] = int(np.sum(vis + win) * H * D * 4)
+        return by, fl
+
+    def unit(self):
+        return "per visible index row: 256 B read (64x128 heads: 16,384 flop)" if self.cfg.csa else \
+            "per attended KV row: 1,024 B read (64 heads x 512: 131,072 flop)"
+
+    def describe(self):
+        cfg = self.cfg
+        d = dict(workload=cfg.name, batch=cfg.B, context=int(cfg.ctx) if not cfg.ctx_lo else
+                 [int(cfg.ctx_lo), int(cfg.ctx)], compressed_entries=int(np.max(self.n_vis)), ratio=cfg.ratio,
+                 heads=cfg.H, head_dim=cfg.D, rope_dim=cfg.rope_dim, window=cfg.window, cache_copies=self.copies)
+        if cfg.csa:
+            d.update(index_heads=cfg.H_I, index_dim=cfg.D_I, top_k=cfg.k)
+        return d
+
+
+class PrefillWorkload:
+    """CSA prefill of S tokens: compress all groups, score, top-k, attention."""
+
+    def __init__(self, cfg, device, copies=2):
+        import torch
+        import compressed_sparse_attention_06_amd as csa
+        self.cfg, self.device = cfg, device
+        S, D, DI = cfg.S, cfg.D, cfg.D_I
+        inp = synth.prefill_inputs(cfg)
+        self.copies = copies
+        self.Nc = S // cfg.ratio
+        self.kv = _bf16(inp["kv"][None], device)
+        self.gate = _bf16(inp["gate"][None], device)
+        self.ki = _bf16(inp["k_idx"][None], device)
+        self.gi = _bf16(inp["g_idx"][None], device)
+        self.win = _bf16(inp["win"][None], device)
+        q = _bf16(inp["q"][None], device)
+        qi = _bf16(inp["q_idx"][None], device)
+        self.q = [q] + [q.clone() for _ in range(copies - 1)]
+        self.q_idx = [qi] + [qi.clone() for _ in range(copies - 1)]
+        self.w = _f32(inp["w"][None], device)
+        shared = synth.decode_shared(cfg)
+        self.sink = _f32(shared["sink"], device)
+        self.gamma = _f32(shared["gamma"], device)
+        self.gamma_idx = _f32(shared["gamma_idx"], device)
+        self.pos = torch.arange(S, dtype=torch.int32, device=device)[None]
+        self.kv_cache = torch.empty((1, self.Nc, D), dtype=torch.bfloat16, device=device)
+        self.idx_cache = torch.empty((1, self.Nc, DI), dtype=torch.bfloat16, device=device)
+        self.scores = torch.empty((1, S, self.Nc), dtype=torch.float32, device=device)
+        self.sel = torch.empty((1, S, cfg.k), dtype=torch.int32, device=device)
+        self.out = torch.empty((1, S, cfg.H, D), dtype=torch.bfloat16, device=device)
+        self.ws_topk = torch.empty(max(1, csa.csa_topk_workspace_size(S, self.Nc, cfg.k)), dtype=torch.uint8,
+                                   device=device)
+        self.ws_attn = torch.empty(max(1, csa.csa_sparse_attn_workspace_size(1, S, cfg.H, D, cfg.k, cfg.window)),
+                                   dtype=torch.uint8, device=device)
+        torch.cuda.synchronize()
+
+    def launches(self, c):
+        import compressed_sparse_attention_06_amd as csa
+        cfg, S = self.cfg, self.cfg.S
+        c = c % self.copies
+        return [
+            ("compress_kv", lambda: csa.csa_compress(self.kv, self.gate, self.gamma, self.kv_cache, ratio=cfg.ratio,
+                                                     overlap=cfg.overlap, rope_dim=cfg.rope_dim, eps=cfg.eps)),
+            ("compress_idx", lambda: csa.csa_compress(self.ki, self.gi, self.gamma_idx, self.idx_cache,
+                                                      ratio=cfg.ratio, overlap=cfg.overlap,
+                                                      rope_dim=cfg.rope_dim_idx, eps=cfg.eps)),
+            ("index_score", lambda: csa.csa_index_score(self.q_idx[c], self.w, self.idx_cache, self.pos,
+                                                        self.scores, ratio=cfg.ratio)),
+            ("topk", lambda: csa.csa_topk(self.scores.view(S, self.Nc), None, cfg.k, self.sel.view(S, cfg.k),
+                                          ws=self.ws_topk)),
+            ("sparse_attn", lambda: csa.csa_sparse_attn(self.q[c], self.kv_cache, self.sel, self.win, self.pos,
+                                                        self.sink, self.out, window=cfg.window,
+                                                        scale=1.0 / math.sqrt(cfg.D), rope_dim=cfg.rope_dim,
+                                                        ws=self.ws_attn)),
+        ]
+
+    def queries(self):
+        return self.cfg.S
+
+    def dominant(self):
+        return "index_score"
+
+    def algorithmic(self):
+        cfg, S = self.cfg, self.cfg.S
+        D, DI, H, HI, r = cfg.D, cfg.D_I, cfg.H, cfg.H_I, cfg.ratio
+        t = np.arange(S)
+        vis = (t + 1) // r
+        win = np.minimum(cfg.window, t + 1)
+        sel = np.minimum(vis, cfg.k)
+        by = {"compress_kv": S * D * 2 * 2 + self.Nc * D * 2, "compress_idx": S * DI * 2 * 2 + self.Nc * DI * 2,
+              "index_score": S * HI * DI * 2 + S * HI * 4 + self.Nc * DI * 2 + S * self.Nc * 4,
+              "topk": S * self.Nc * 4 + S * cfg.k * 4,
+              "sparse_attn": int(S * H * D * 2 * 2 + np.sum(sel + win) * D * 2 + S * cfg.k * 4)}
+        fl = {"index_score": int(np.sum(vis)) * HI * DI * 2, "sparse_attn": int(np.sum(sel + win)) * H * D * 4}
+        return by, fl
+
+    def unit(self):
+        return "per visible (query, entry) pair: 64 heads x 128 dims = 16,384 flop"
+
+    def describe(self):
+        cfg = self.cfg
+        return dict(workload=cfg.name, batch=1, tokens=cfg.S, compressed_entries=self.Nc, ratio=cfg.ratio,
+                    heads=cfg.H, head_dim=cfg.D, index_heads=cfg.H_I, index_dim=cfg.D_I, top_k=cfg.k,
+                    window=cfg.window, query_copies=self.copies)
+
+
+def make_workload(name, device):
+    cfg = synth.CONFIGS[name]
+    if cfg.kind == "decode":
+        return DecodeWorkload(cfg, device)
+    if cfg.kind == "prefill":
+        return PrefillWorkload(cfg, device)
+    raise SystemExit(f"{name} is a parity-test configuration, not a bench workload")
+
+
+# ---------------------------------------------------------------------------
+# Timing
+# ---------------------------------------------------------------------------
+def _spin(ms):
+    """Keep the GPU busy for about `ms` so that what follows is queued back to back."""
+    import torch
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(int(ms * 1e-3 * 2.4e9))
+
+
+def capture_graphs(wl, n, only=None):
+    import torch
+    graphs = []
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for c in range(n):
+            for name, fn in wl.launches(c):
+                if only is None or name == only:
+                    fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for c in range(n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for name, fn in wl.launches(c):
+                if only is None or name == only:
+                    fn()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def time_steps(wl, steps, warmup, only=None):
+    """Replay `steps` one-step graphs between events; returns per-step ms."""
+    import torch
+    graphs = capture_graphs(wl, min(wl.copies, max(steps, 1)), only)
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    _spin(20)
+    ev[0].record()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    total = ev[0].elapsed_time(ev[steps])
+    return per, total
+
+
+def time_kernels(wl, steps):
+    """Per-kernel durations (ms) from HIP events around each eager launch."""
+    import torch
+    names = [n for n, _ in wl.launches(0)]
+    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+          for n in names}
+    for i in range(2):
+        for _, fn in wl.launches(i):
+            fn()
+    torch.cuda.synchronize()
+    _spin(60)
+    for i in range(steps):
+        for n, fn in wl.launches(i):
+            a, b = ev[n][i]
+            a.record()
+            fn()
+            b.record()
+    torch.cuda.synchronize()
+    return {n: np.array([a.elapsed_time(b) for a, b in ev[n]]) for n in names}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the float64 oracle on a bounded sample of the same workload
+# ---------------------------------------------------------------------------
+def cpu_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline_decode(wl, seconds):
+    import oracle
+    from oracle import pipeline
+    cfg = wl.cfg
+    f64 = synth.bf16_to_f64
+    shared = synth.decode_shared(cfg)
+    prepared = []
+    for s in wl.seqs:
+        d = dict(seq=s)
+        d["kv"] = f64(synth.kv_cache_rows(cfg, s.b, s.n_vis))
+        if cfg.csa:
+            d["idx"] = f64(synth.idx_cache_rows(cfg, s.b, s.n_vis))
+        prepared.append(d)
+        if len(prepared) * s.n_vis > 2_000_000:
+            break
+
+    def one(d):
+        s = d["seq"]
+        e = s.n_vis - 1
+        scale = 1.0 / math.sqrt(cfg.D)
+        emit = (s.pos + 1) % cfg.ratio == 0
+        prev, cur = oracle.entry_candidates(e, cfg.ratio, cfg.overlap)
+        toks = prev + cur                     # staging ring slot = token % R
+        if emit:
+            rows = lambda st: f64(st[[t % wl.R for t in toks]])
+            d["kv"][e] = oracle.entry_from_rows(e, cfg.ratio, rows(s.gate_stage), rows(s.kv_stage), shared["gamma"],
+                                                cfg.rope_dim, cfg.rope_base, cfg.eps)
+        win = np.stack([f64(s.win[p % cfg.window]) for p in oracle.window_positions(s.pos, cfg.window)])
+        q = f64(s.q)
+        if cfg.csa:
+            if emit:
+                d["idx"][e] = oracle.entry_from_rows(e, cfg.ratio, rows(s.gi_stage), rows(s.ki_stage),
+                                                     shared["gamma_idx"], cfg.rope_dim_idx, cfg.rope_base, cfg.eps)
+            pipeline.csa_query(q, f64(s.q_idx), s.w, d["kv"], d["idx"], s.n_vis, win, shared["sink"], cfg.k,
+                               scale, s.pos, cfg.rope_dim, cfg.rope_base)
+        else:
+            oracle.hca_attn(q, d["kv"], s.n_vis, win, shared["sink"], scale, s.pos, cfg.rope_dim, cfg.rope_base)
+
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        one(prepared[n % len(prepared)])
+        n += 1
+    dt = time.perf_counter() - t0
+    return dict(value=n / dt, unit="query-tokens/s", cores=cpu_threads(), kind="oracle",
+                sample=f"{n} decode queries of {cfg.name} (sequences 0..{len(prepared) - 1} in turn, float64 "
+                       f"NumPy oracle: compress the completed group, score, top-k, attend), {dt:.1f} s")
+
+
+def cpu_baseline_prefill(wl, seconds):
+    import oracle
+    from oracle import pipeline
+    cfg = wl.cfg
+    f64 = synth.bf16_to_f64
+    shared = synth.decode_shared(cfg)
+    inp = synth.prefill_inputs(cfg, q_rows=np.arange(cfg.S - 256, cfg.S))
+    t0 = time.perf_counter()
+    kvc = oracle.compress(f64(inp["kv"]), f64(inp["gate"]), shared["gamma"], cfg.ratio, cfg.overlap, cfg.rope_dim)
+    idc = oracle.compress(f64(inp["k_idx"]), f64(inp["g_idx"]), shared["gamma_idx"], cfg.ratio, cfg.overlap,
+                          cfg.rope_dim_idx)
+    win = f64(inp["win"])
+    n = 0
+    qs = np.arange(cfg.S - 256, cfg.S)
+    while time.perf_counter() - t0 < seconds and n < qs.size:
+        t = int(qs[n])
+        pipeline.csa_query(f64(inp["q"][n]), f64(inp["q_idx"][n]), inp["w"][n], kvc, idc, oracle.visible(t, 4),
+                           pipeline.window_rows(win, t, cfg.window), shared["sink"], cfg.k, 1 / math.sqrt(cfg.D),
+                           t, cfg.rope_dim)
+        n += 1
+    dt = time.perf_counter() - t0
+    return dict(value=n / dt, unit="query-tokens/s", cores=cpu_threads(), kind="oracle",
+                sample=f"compress all {cfg.S} tokens (both roles) + {n} of the last 256 queries of {cfg.name} "
+                       f"(score 2048 entries, top-k, attend), float64 NumPy oracle, {dt:.1f} s")
+
+
+# ---------------------------------------------------------------------------
+def measure(wl, steps, warmup, only=None):
+    per, total = time_steps(wl, steps, warmup, only)
+    ms = total / steps
+    kern = time_kernels(wl, steps)
+    by, fl = wl.algorithmic()
+    dom = wl.dominant()
+    dom_ms = float(np.mean(kern[dom]))
+    res = dict(ms_per_step=ms, per=per, kern={n: float(np.mean(v)) * 1e3 for n, v in kern.items()},
+               step_bytes=int(sum(by.values())), by=by, fl=fl, dom=dom, dom_ms=dom_ms)
+    return res
+
+
+def roofline(wl, m):
+    dom, t = m["dom"], m["dom_ms"] * 1e-3
+    if isinstance(wl, PrefillWorkload):
+        ach = m["fl"][dom] / t / 1e12
+        return dict(bound="mfma", achieved=round(ach, 2), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(ach / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None, kernel=dom,
+                    kernel_us=round(m["dom_ms"] * 1e3, 2), algorithmic_flops=m["fl"][dom], per_unit=wl.unit())
+    ach = m["by"][dom] / t / 1e9
+    return dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4),
+                traffic=None, kernel=dom, kernel_us=round(m["dom_ms"] * 1e3, 2), algorithmic_bytes=m["by"][dom],
+                per_unit=wl.unit())
+
+
+def summary(wl, m):
+    q = wl.queries()
+    per = m["per"] * 1e3
+    return dict(query_tokens_per_s=round(q / (m["ms_per_step"] * 1e-3), 1), ms_per_step=round(m["ms_per_step"], 5),
+                step_us_p50=round(float(np.percentile(per, 50)), 2), step_us_p95=round(float(np.percentile(per, 95)), 2),
+                step_us_p99=round(float(np.percentile(per, 99)), 2),
+                hbm_gbs_step=round(m["step_bytes"] / (m["ms_per_step"] * 1e-3) / 1e9, 1),
+                kernels_us={n: round(v, 2) for n, v in m["kern"].items()}, roofline=roofline(wl, m),
+                config=wl.describe())
+
+
+def note(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this path runs on a single MI355X (see the sharding notes in the design "
+              "document); --gpus above 1 is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import compressed_sparse_attention_06_amd as csa
+    csa.lib()
+    dev = torch.device("cuda:0")
+    t_setup = time.time()
+    wl = make_workload(args.workload, dev)
+    setup_s = time.time() - t_setup
+    note(f"{args.workload}: inputs resident in HBM after {setup_s:.1f} s")
+    only = args.kernel_only or None
+    m = measure(wl, args.steps, args.warmup, only)
+    note(f"{args.workload}: {m['ms_per_step'] * 1e3:.2f} us/step")
+    main_sum = summary(wl, m)
+    line = dict(metric=METRIC, value=main_sum["query_tokens_per_s"], unit="query-tokens/s", n_gpus=1,
+                steps=args.steps, warmup=args.warmup, ms_per_step=main_sum["ms_per_step"], higher_is_better=True,
+                scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic", config=main_sum["config"],
+                roofline=main_sum["roofline"])
+    for key in ("hbm_gbs_step", "step_us_p50", "step_us_p95", "step_us_p99", "kernels_us"):
+        line[key] = main_sum[key]
+    line["setup_s"] = round(setup_s, 1)
+    if not args.no_cpu_baseline:
+        if isinstance(wl, PrefillWorkload):
+            line["cpu_baseline"] = cpu_baseline_prefill(wl, args.cpu_seconds)
+        else:
+            line["cpu_baseline"] = cpu_baseline_decode(wl, args.cpu_seconds)
+        note(f"cpu baseline: {line['cpu_baseline']['value']:.2f} {line['cpu_baseline']['unit']}")
+    del wl
+    torch.cuda.empty_cache()
+    extras = {}
+    for name in [x for x in args.extra.split(",") if x and x != args.workload]:
+        w2 = make_workload(name, dev)
+        note(f"{name}: inputs resident")
+        m2 = measure(w2, args.steps, args.warmup)
+        note(f"{name}: {m2['ms_per_step'] * 1e3:.2f} us/step")
+        extras[name] = summary(w2, m2)
+        if isinstance(w2, PrefillWorkload):
+            extras[name]["indexer_mfma_util"] = extras[name]["roofline"]["frac"]
+        del w2
+        torch.cuda.empty_cache()
+    if extras:
+        line["secondary"] = extras
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -5,6 +5,6 @@ benchmark's CPU-baseline leg, never by the product path.  It shares no code
 with the HIP library and imports nothing from it.
 """
 from . import csa, pipeline  # noqa: F401
-from .csa import (NEG_INF, attend, compress, compress_entry, entry_candidates, hca_attn,  # noqa: F401
+from .csa import (NEG_INF, attend, compress, compress_entry, entry_candidates, entry_from_rows, hca_attn,  # noqa: F401
                   index_score, pool, rms_norm, rope, sparse_attn, topk, visible,
                   window_positions, StreamingCompressor)

@@ -139,7 +139,16 @@ def compress_entry(e, kv, gate, kv_prev, gate_prev, gamma, ratio, overlap,
     prev, cur = entry_candidates(e, ratio, overlap)
     g = [gate_prev[t] for t in prev] + [gate[t] for t in cur]
     v = [kv_prev[t] for t in prev] + [kv[t] for t in cur]
-    y = pool(np.stack(g), np.stack(v))
+    return entry_from_rows(e, ratio, np.stack(g), np.stack(v), gamma, rope_dim, rope_base, eps)
+
+
+def entry_from_rows(e, ratio, gates, values, gamma, rope_dim, rope_base=10000.0, eps=1e-6):
+    """Entry e from its candidate rows (previous group first, then current).
+
+    Pool, RMSNorm, then RoPE at the entry position e*ratio
+    [V4-Flash walkthrough, "压缩是逐通道的 learned pooling"].
+    """
+    y = pool(gates, values)
     y = rms_norm(y, gamma, eps)
     return rope(y, e * ratio, rope_dim, rope_base)
 
