@@ -50,7 +50,22 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-only", default="", help="profiling aid: replay only this kernel's graphs")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="counter reference: copy MIB MiB device-to-device 8 times and exit")
     return ap.parse_args()
+
+
+def copy_probe(mib):
+    """A plain copy of known size, to scale the HBM byte counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(8):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_per_copy": n * 4, "copies": 8}), flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -117,6 +132,12 @@ class DecodeWorkload:
             self.ws_attn = torch.empty(max(1, csa.hca_attn_workspace_size(B, 1, cfg.H, D, self.Ncap, cfg.window)),
                                        dtype=torch.uint8, device=device)
         torch.cuda.synchronize()
+
+    @property
+    def side_kernels(self):
+        return ("compress_kv",) if self.cfg.csa else ()
+
+    join_before = "sparse_attn"
 
     # the kernels of one step, as (name, callable) in launch order
     def launches(self, c):
@@ -296,24 +317,48 @@ def _spin(ms):
         torch.cuda._sleep(int(ms * 1e-3 * 2.4e9))
 
 
+def run_step(wl, c, only=None, side=None):
+    """Enqueue one step.  Kernels the workload marks independent (the KV-role
+    compressor of a CSA decode step, needed only by the attention) go to the
+    `side` stream and are joined back before the first kernel that reads them."""
+    import torch
+    launches = wl.launches(c)
+    forked = [n for n in getattr(wl, "side_kernels", ()) if only is None]
+    if side is None or not forked:
+        for name, fn in launches:
+            if only is None or name == only:
+                fn()
+        return
+    main = torch.cuda.current_stream()
+    side.wait_stream(main)
+    with torch.cuda.stream(side):
+        for name, fn in launches:
+            if name in forked:
+                fn()
+    for name, fn in launches:
+        if name in forked:
+            continue
+        if name == wl.join_before:
+            main.wait_stream(side)
+        fn()
+
+
 def capture_graphs(wl, n, only=None):
     import torch
     graphs = []
+    side = torch.cuda.Stream()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         for c in range(n):
-            for name, fn in wl.launches(c):
-                if only is None or name == only:
-                    fn()
+            run_step(wl, c, only, side)
+        s.wait_stream(side)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     for c in range(n):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for name, fn in wl.launches(c):
-                if only is None or name == only:
-                    fn()
+            run_step(wl, c, only, side)
         graphs.append(g)
     torch.cuda.synchronize()
     return graphs
@@ -498,6 +543,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     import compressed_sparse_attention_06_amd as csa
     csa.lib()
     dev = torch.device("cuda:0")

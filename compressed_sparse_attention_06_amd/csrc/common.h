@@ -66,18 +66,29 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // ---------------------------------------------------------------------------
-// RoPE angle of pair i at position p: p * base^(-2i/rope_dim), formed and
-// range-reduced in double so that positions near 2^20 keep full accuracy.
+// RoPE angle of pair i at position p: p * base^(-2i/rope_dim).  The angle is
+// formed in double and reduced modulo 2*pi with a two-term Cody-Waite split
+// of 2*pi (head = nearest double, tail = the remainder), so positions near
+// 2^20 keep full accuracy; the reduced angle in [-pi, pi] then goes through
+// a single-precision sincos.
 // ---------------------------------------------------------------------------
+constexpr double kTwoPiHi = 6.283185307179586;
+constexpr double kTwoPiLo = 2.4492935982947064e-16;
+
 __device__ __forceinline__ void rope_cos_sin(int64_t p, int i, int rope_dim, float base,
                                              float* c, float* s) {
-  double theta = exp2(-2.0 * double(i) / double(rope_dim) * log2(double(base)));
-  double sn, cs;
-  sincos(double(p) * theta, &sn, &cs);
-  *c = float(cs);
-  *s = float(sn);
+  const double theta = exp2(-2.0 * double(i) / double(rope_dim) * log2(double(base)));
+  const double x = double(p) * theta;
+  const double k = rint(x * (1.0 / kTwoPiHi));
+  double r = fma(-k, kTwoPiHi, x);
+  r = fma(-k, kTwoPiLo, r);
+  sincosf(float(r), s, c);
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// 2^x on the hardware exponential (v_exp_f32).  Softmax arguments here are
+// <= 0; results below 2^-126 flush to zero, which is harmless for weights.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 }  // namespace csa

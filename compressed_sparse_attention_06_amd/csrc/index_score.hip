@@ -11,15 +11,15 @@
 //
 //  * index_stream (few queries, e.g. decode): each wave keeps the query's
 //    64x128 operand in registers and streams 64 index rows per step straight
-//    from HBM into registers (each lane reads 64 contiguous bytes of one row),
-//    4 x 16x16x32 MFMA per 16 rows and K-step, then ReLU, head weights and a
-//    two-step cross-lane sum.  Pure streaming: no LDS.
+//    from HBM into registers (every load instruction covers 64 contiguous
+//    bytes of 16 rows), 4 x 16x16x32 MFMA per 16 rows and K-step, then ReLU,
+//    head weights and a two-step cross-lane sum.
 //  * index_tile (many queries, e.g. prefill): a workgroup keeps a tile of
 //    index rows stationary in registers and streams query operands through
 //    LDS; causal tiles that no query of the block can see are skipped.
 //
-// Both use the same K-order inside an MFMA K-step (lane group g, element i
-// <-> dim g*32 + ks*8 + i) for A and B, which the contraction allows.
+// A and B share the K order of a K-step: lane group g, element i <-> dim
+// ks*32 + g*8 + i.
 #include "common.h"
 #include "kernels.h"
 
@@ -36,77 +36,109 @@ __device__ __forceinline__ int64_t visible_entries(const int* pos, int64_t qi, i
 }
 
 // ---------------------------------------------------------------------------
-// Streaming kernel: grid (ceil(Ncap / 256), B*S), 4 waves x 64 entries.
+// Streaming kernel: grid (B*S, ceil(Ncap / (512*STEPS))), 8 waves.
+// Block rows come in steps of 512 (64 per wave); step s+1 is loaded while
+// step s is multiplied.  The query operand (16 KiB) is staged once per block
+// in LDS and then held in VGPRs by every wave.
 // ---------------------------------------------------------------------------
-constexpr int kStreamWaves = 4;
-constexpr int kStreamRows = 64;  // rows per wave
-constexpr int kStreamBlockRows = kStreamWaves * kStreamRows;
+constexpr int kStreamWaves = 8;
+constexpr int kStepRows = kStreamWaves * 64;
 
+template <int STEPS>
 __global__ __launch_bounds__(kWave* kStreamWaves) void index_stream(IndexArgs a) {
+  __shared__ uint4 qs[kHI * kDI / 8];
+  __shared__ float wsh[kHI];
   const int64_t qi = blockIdx.x;
   const int b = int(qi / a.S);
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int g = lane / 16, r16 = lane % 16;
   const int Ncap = a.Ncap;
   const int64_t n_vis = visible_entries(a.pos, qi, a.ratio, Ncap);
-  const int64_t e_base = int64_t(blockIdx.y) * kStreamBlockRows + wave * kStreamRows;
+  const int64_t row0 = int64_t(blockIdx.y) * kStepRows * STEPS;
   float* srow = a.scores + qi * Ncap;
 
-  if (e_base >= n_vis) {  // nothing visible in this wave's rows
-    const int64_t e = e_base + lane;
-    if (e < Ncap) srow[e] = -INFINITY;
+  if (row0 >= n_vis) {  // nothing visible in this block
+    for (int64_t e = row0 + tid; e < row0 + int64_t(kStepRows) * STEPS && e < Ncap; e += kWave * kStreamWaves)
+      srow[e] = -INFINITY;
     return;
   }
-
-  const uint16_t* q = static_cast<const uint16_t*>(a.q_idx) + qi * (kHI * kDI);
-  bf16x8 qa[4][4];  // [head tile][K-step]
+  const uint16_t* cache = static_cast<const uint16_t*>(a.cache) + int64_t(b) * Ncap * kDI;
+  // per 16-row block and K-step, lane (g, r16) reads row r16, bytes ks*64 + g*16:
+  // every load instruction covers 64 contiguous bytes of 16 rows
+  auto load = [&](int step, uint4 (&kb)[4][4]) {
+    const int64_t base = row0 + int64_t(step) * kStepRows + wave * 64;
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      const int64_t e = base + blk * 16 + r16;
+      if (e < n_vis) {
+        const uint4* src = reinterpret_cast<const uint4*>(cache + e * kDI) + g;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kb[blk][ks] = src[ks * 4];
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kb[blk][ks] = uint4{0, 0, 0, 0};
+      }
+    }
+  };
+  // the first step's rows are requested before the query operand is staged
+  uint4 kb0[4][4];
+  load(0, kb0);
+  {
+    const uint4* q = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q_idx) + qi * (kHI * kDI));
+    for (int i = tid; i < kHI * kDI / 8; i += kWave * kStreamWaves) qs[i] = q[i];
+    if (tid < kHI) wsh[tid] = a.w[qi * kHI + tid];
+  }
+  __syncthreads();
+  bf16x8 qa[4][4];  // [head tile][K-step]: Q[mt*16 + r16][ks*32 + g*8 .. +7]
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      qa[mt][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(q + (mt * 16 + r16) * kDI + g * 32 + ks * 8));
+    for (int ks = 0; ks < 4; ++ks) qa[mt][ks] = as_bf16x8(qs[(mt * 16 + r16) * (kDI / 8) + ks * 4 + g]);
   float wv[4][4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wv[mt][i] = a.w[qi * kHI + mt * 16 + g * 4 + i];
+    for (int i = 0; i < 4; ++i) wv[mt][i] = wsh[mt * 16 + g * 4 + i];
 
-  const uint16_t* cache = static_cast<const uint16_t*>(a.cache) + int64_t(b) * Ncap * kDI;
-  uint4 kb[4][4];  // [16-row block][K-step]
+  auto score = [&](int step, const uint4 (&kb)[4][4]) {
+    const int64_t base = row0 + int64_t(step) * kStepRows + wave * 64;
 #pragma unroll
-  for (int blk = 0; blk < 4; ++blk) {
-    const int64_t e = e_base + blk * 16 + r16;
-    if (e < n_vis) {
-      const uint4* src = reinterpret_cast<const uint4*>(cache + e * kDI + g * 32);
+    for (int blk = 0; blk < 4; ++blk) {
+      floatx4 acc[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kb[blk][ks] = src[ks];
-    } else {
+      for (int mt = 0; mt < 4; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kb[blk][ks] = uint4{0, 0, 0, 0};
-    }
-  }
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 kk = as_bf16x8(kb[blk][ks]);
 #pragma unroll
-  for (int blk = 0; blk < 4; ++blk) {
-    floatx4 acc[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 kk = as_bf16x8(kb[blk][ks]);
+        for (int mt = 0; mt < 4; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][ks], kk, acc[mt], 0, 0, 0);
+      }
+      // lane holds heads mt*16 + g*4 + i of row r16
+      float part = 0.f;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][ks], kk, acc[mt], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part += fmaxf(acc[mt][i], 0.f) * wv[mt][i];
+      part += __shfl_xor(part, 16, kWave);
+      part += __shfl_xor(part, 32, kWave);
+      const int64_t e = base + blk * 16 + r16;
+      if (g == 0 && e < Ncap) srow[e] = e < n_vis ? part : -INFINITY;
     }
-    // lane holds heads mt*16 + g*4 + i of row r16
-    float part = 0.f;
+  };
+  if constexpr (STEPS == 1) {
+    score(0, kb0);
+  } else {
+    uint4 kb1[4][4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) part += fmaxf(acc[mt][i], 0.f) * wv[mt][i];
-    part += __shfl_xor(part, 16, kWave);
-    part += __shfl_xor(part, 32, kWave);
-    const int64_t e = e_base + blk * 16 + r16;
-    if (g == 0 && e < Ncap) srow[e] = e < n_vis ? part : -INFINITY;
+    for (int s = 0; s < STEPS; s += 2) {
+      if (s + 1 < STEPS) load(s + 1, kb1);
+      score(s, kb0);
+      if (s + 1 < STEPS) {
+        if (s + 2 < STEPS) load(s + 2, kb0);
+        score(s + 1, kb1);
+      }
+    }
   }
 }
 
@@ -143,8 +175,15 @@ hipError_t launch_index_score(const IndexArgs& a, hipStream_t stream) {
   const int64_t nq = int64_t(a.B) * a.S;
   if (nq == 0 || a.Ncap == 0) return hipSuccess;
   if (a.use_mfma && a.H == kHI && a.D == kDI) {
-    const dim3 grid(unsigned(nq), (a.Ncap + kStreamBlockRows - 1) / kStreamBlockRows);
-    hipLaunchKernelGGL(index_stream, grid, dim3(kWave * kStreamWaves), 0, stream, a);
+    const int64_t blocks1 = nq * ((a.Ncap + kStepRows - 1) / kStepRows);
+    if (blocks1 <= 4096) {
+      const dim3 grid(unsigned(nq), (a.Ncap + kStepRows - 1) / kStepRows);
+      hipLaunchKernelGGL(index_stream<1>, grid, dim3(kWave * kStreamWaves), 0, stream, a);
+    } else {
+      constexpr int kSteps = 4;
+      const dim3 grid(unsigned(nq), (a.Ncap + kStepRows * kSteps - 1) / (kStepRows * kSteps));
+      hipLaunchKernelGGL(index_stream<kSteps>, grid, dim3(kWave * kStreamWaves), 0, stream, a);
+    }
   } else {
     const dim3 grid(unsigned(nq), (a.Ncap + 255) / 256);
     hipLaunchKernelGGL(index_any, grid, dim3(256), (a.H * a.D + a.H) * sizeof(float), stream, a);

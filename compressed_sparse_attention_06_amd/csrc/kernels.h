@@ -75,7 +75,7 @@ struct AttnPlan {
   int chunk_rows;
   size_t ws_bytes;
 };
-AttnPlan plan_attn(int B, int S, int H, int D, int max_cand, int dtype);
+AttnPlan plan_attn(int B, int S, int H, int D, int max_cand, int dtype, bool hca);
 hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, bool hca, hipStream_t stream);
 
 }  // namespace csa

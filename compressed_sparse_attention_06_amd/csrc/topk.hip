@@ -6,9 +6,14 @@
 //
 // Scores map to order-preserving 32-bit keys (invisible / -inf -> 0).  A
 // workgroup stages up to M keys of one row in LDS and finds the exact k-th
-// largest key with four 8-bit radix passes (LDS histogram, suffix scan).  The
-// kept set is then written by an ordered compaction: every thread owns a
-// contiguous run of positions, two block scans give each thread its output
+// largest key with few barriers: a histogram over 256 equal-width score bins
+// (built straight from registers into per-wave LDS histograms) locates the
+// bin of the k-th score, one wave scans the bins, the keys of that bin are
+// gathered into a short list and ranked against each other, which yields
+// the exact threshold key (8-bit radix passes over the bin remain as the
+// fallback for heavily tied data).  The kept set is then written by an
+// ordered compaction: every thread owns a contiguous run of positions, one
+// block scan of packed (greater, equal) counts gives each thread its output
 // offset and its share of the threshold-equal keys, so ties go to the lowest
 // index and the output is sorted by index -- deterministic run to run.
 //
@@ -30,6 +35,23 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   if (f == -INFINITY) return 0u;
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Score value of a valid key (inverse of score_key).
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
+  return v;
 }
 
 // Exclusive scan over the block; returns the exclusive prefix, *total the sum.
@@ -73,92 +95,225 @@ struct SelectArgs {
 template <int THREADS, int ITEMS, bool FROM_CAND, bool FINAL>
 __global__ __launch_bounds__(THREADS) void topk_select(SelectArgs a) {
   constexpr int M = THREADS * ITEMS;
-  __shared__ uint32_t keys[M];
-  __shared__ int idxs[FROM_CAND ? M : 1];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t wsum[THREADS / kWave + 1];
+  constexpr int W = THREADS / kWave;
+  __shared__ __attribute__((aligned(16))) uint32_t keys[M];
+  __shared__ __attribute__((aligned(16))) int idxs[FROM_CAND ? M : 1];
+  __shared__ uint32_t hist[W][256];  // one histogram per wave: no cross-wave atomic contention
+  __shared__ uint32_t wsum[W + 1];
+  __shared__ uint32_t wcount[W];
+  __shared__ float wlo[W], whi[W];
+  __shared__ uint32_t list[THREADS];  // keys of the threshold bin
+  __shared__ uint32_t nlist, sh_bin, sh_above, sh_thr, sh_need;
   __shared__ uint32_t pick[2];
 
   const int row = blockIdx.x, chunk = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid % kWave, wave = tid / kWave;
   const int64_t base = int64_t(chunk) * M;
   int len = a.in_len;
   if (!FROM_CAND && a.n_valid != nullptr) len = min(len, max(a.n_valid[row], 0));
+  for (int i = lane; i < 256; i += kWave) hist[wave][i] = 0;  // own wave's histogram
+  if (tid == 0) nlist = 0;
 
-  uint32_t ok = 0;
-  for (int j = tid; j < M; j += THREADS) {
-    const int64_t p = base + j;
-    uint32_t key = 0;
-    if (p < len) {
-      if constexpr (FROM_CAND) {
-        key = a.ckey[int64_t(row) * a.in_len + p];
-        idxs[j] = a.cidx[int64_t(row) * a.in_len + p];
-      } else {
-        key = score_key(a.scores[int64_t(row) * a.in_len + p]);
+  // Coalesced, straight-line loads (position tid + t*THREADS); the keys then
+  // pass once through LDS so that every thread owns the contiguous run
+  // [tid*ITEMS, tid*ITEMS + ITEMS) in registers for the rest of the kernel.
+  {
+    uint32_t kin[ITEMS];
+    int iin[FROM_CAND ? ITEMS : 1];
+    const int64_t rbase = int64_t(row) * a.in_len;
+    if (base < len) {
+      const int64_t last = len - 1;
+#pragma unroll
+      for (int t = 0; t < ITEMS; ++t) {
+        const int64_t p = base + tid + t * THREADS;
+        const int64_t q = p < last ? p : last;
+        if constexpr (FROM_CAND) {
+          kin[t] = a.ckey[rbase + q];
+          iin[t] = a.cidx[rbase + q];
+        } else {
+          kin[t] = __float_as_uint(a.scores[rbase + q]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < ITEMS; ++t) {
+        const bool in = base + tid + t * THREADS < len;
+        if constexpr (FROM_CAND) kin[t] = in ? kin[t] : 0u;
+        else kin[t] = in ? score_key(__uint_as_float(kin[t])) : 0u;
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < ITEMS; ++t) {
+        kin[t] = 0u;
+        if constexpr (FROM_CAND) iin[t] = -1;
       }
     }
-    keys[j] = key;
-    ok += key != 0u;
+#pragma unroll
+    for (int t = 0; t < ITEMS; ++t) {
+      keys[tid + t * THREADS] = kin[t];
+      if constexpr (FROM_CAND) idxs[tid + t * THREADS] = iin[t];
+    }
   }
-  uint32_t n_ok;
-  block_scan<THREADS>(ok, wsum, &n_ok);  // also orders the LDS fills
+  __syncthreads();
+  uint32_t key[ITEMS];
+  int kidx[FROM_CAND ? ITEMS : 1];
+#pragma unroll
+  for (int t = 0; t < ITEMS; t += 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(&keys[tid * ITEMS + t]);
+    key[t] = v.x; key[t + 1] = v.y; key[t + 2] = v.z; key[t + 3] = v.w;
+    if constexpr (FROM_CAND) {
+      const int4 w = *reinterpret_cast<const int4*>(&idxs[tid * ITEMS + t]);
+      kidx[t] = w.x; kidx[t + 1] = w.y; kidx[t + 2] = w.z; kidx[t + 3] = w.w;
+    }
+  }
+  uint32_t ok = 0;
+  float lo = INFINITY, hi = -INFINITY;  // score range of the valid keys
+#pragma unroll
+  for (int t = 0; t < ITEMS; ++t) {
+    if (key[t] != 0u) {
+      const float f = key_value(key[t]);
+      ++ok;
+      lo = fminf(lo, f);
+      hi = fmaxf(hi, f);
+    }
+  }
+  ok = wave_sum_u32(ok);
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  if (lane == 0) { wcount[wave] = ok; wlo[wave] = lo; whi[wave] = hi; }
+  __syncthreads();
+  uint32_t n_ok = 0;
+#pragma unroll
+  for (int w = 0; w < W; ++w) { n_ok += wcount[w]; lo = fminf(lo, wlo[w]); hi = fmaxf(hi, whi[w]); }
 
   uint32_t thr = 0, need_eq = 0;
   if (n_ok > uint32_t(a.k)) {
-    uint32_t prefix = 0, mask = 0, remaining = a.k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = tid; i < 256; i += THREADS) hist[i] = 0;
-      __syncthreads();
-      for (int j = tid; j < M; j += THREADS) {
-        const uint32_t key = keys[j];
-        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    // 256 equal-width bins of the score value between the smallest and the
+    // largest score: a monotone function of the score, so higher bins hold
+    // larger keys, and the bins spread the scores out (the top key bits --
+    // sign and exponent -- do not).
+    const float inv = hi > lo ? 256.f / (hi - lo) : 0.f;
+    auto bin = [&](uint32_t key) -> uint32_t {
+      const uint32_t x = uint32_t((key_value(key) - lo) * inv);
+      return x < 255u ? x : 255u;
+    };
+#pragma unroll
+    for (int t = 0; t < ITEMS; ++t)
+      if (key[t] != 0u) atomicAdd(&hist[wave][bin(key[t])], 1u);
+    __syncthreads();
+    // one wave scans the bins from the top: lane L covers bins 255-4L .. 252-4L
+    if (wave == 0) {
+      uint32_t cnt[4], own = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        cnt[j] = 0;
+#pragma unroll
+        for (int w = 0; w < W; ++w) cnt[j] += hist[w][255 - 4 * lane - j];
+        own += cnt[j];
       }
-      __syncthreads();
-      // suffix counts: cum[d] = #keys with this digit >= d
-      const uint32_t hv = tid < 256 ? hist[255 - tid] : 0u;
-      uint32_t tot;
-      const uint32_t ex = block_scan<THREADS>(hv, wsum, &tot);
-      if (tid < 256) {
-        const int d = 255 - tid;
-        const uint32_t above = ex, incl = ex + hv;  // digits > d, digits >= d
-        if (incl >= remaining && above < remaining) { pick[0] = uint32_t(d); pick[1] = above; }
+      uint32_t incl = own;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t y = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += y;
       }
-      __syncthreads();
-      remaining -= pick[1];
-      prefix |= pick[0] << shift;
-      mask |= 0xffu << shift;
-      __syncthreads();
+      uint32_t above = incl - own;  // keys in bins above this lane's
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (above < uint32_t(a.k) && above + cnt[j] >= uint32_t(a.k)) { sh_bin = 255 - 4 * lane - j; sh_above = above; }
+        above += cnt[j];
+      }
     }
-    thr = prefix;
-    need_eq = remaining;
+    __syncthreads();
+    const uint32_t sel_bin = sh_bin;
+    uint32_t remaining = a.k - sh_above;  // how many keys of that bin are kept
+#pragma unroll
+    for (int t = 0; t < ITEMS; ++t) {
+      if (key[t] != 0u && bin(key[t]) == sel_bin) {
+        const uint32_t at = atomicAdd(&nlist, 1u);
+        if (at < THREADS) list[at] = key[t];
+      }
+    }
+    __syncthreads();
+    const uint32_t n = nlist;
+    if (n <= THREADS) {
+      // rank every key of the bin against the others: the threshold key has
+      // fewer than `remaining` larger keys and at least `remaining` >= keys
+      if (tid < int(n)) {
+        const uint32_t key = list[tid];
+        uint32_t gt = 0, eqc = 0;
+        for (uint32_t j = 0; j < n; ++j) {
+          const uint32_t kj = list[j];
+          gt += kj > key;
+          eqc += kj == key;
+        }
+        if (gt < remaining && remaining <= gt + eqc) { sh_thr = key; sh_need = remaining - gt; }
+      }
+      __syncthreads();
+      thr = sh_thr;
+      need_eq = sh_need;
+    } else {
+      // many equal or nearly equal scores: exact 8-bit radix passes over the bin
+      uint32_t prefix = 0, mask = 0;
+      for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = tid; i < W * 256; i += THREADS) (&hist[0][0])[i] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < ITEMS; ++t) {
+          const uint32_t kk = key[t];
+          if (kk != 0u && (kk & mask) == prefix && bin(kk) == sel_bin)
+            atomicAdd(&hist[wave][(kk >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        uint32_t hv = 0;
+        if (tid < 256) {
+#pragma unroll
+          for (int w = 0; w < W; ++w) hv += hist[w][255 - tid];
+        }
+        uint32_t tot;
+        const uint32_t ex = block_scan<THREADS>(hv, wsum, &tot);
+        if (tid < 256 && ex + hv >= remaining && ex < remaining) { pick[0] = uint32_t(255 - tid); pick[1] = ex; }
+        __syncthreads();
+        remaining -= pick[1];
+        prefix |= pick[0] << shift;
+        mask |= 0xffu << shift;
+        __syncthreads();
+      }
+      thr = prefix;
+      need_eq = remaining;
+    }
   }
 
-  // ordered compaction over contiguous runs of ITEMS positions
+  // Ordered compaction over contiguous runs of ITEMS positions.  One scan of
+  // packed (greater, equal) counts gives each thread its output offset: the
+  // equal keys before it that are kept number min(prefix_eq, need_eq).
   const int j0 = tid * ITEMS;
   uint32_t gt = 0, eq = 0;
 #pragma unroll
   for (int t = 0; t < ITEMS; ++t) {
-    const uint32_t key = keys[j0 + t];
-    gt += key > thr;
-    eq += (key == thr) && (key != 0u);
+    gt += key[t] > thr;
+    eq += (key[t] == thr) && (key[t] != 0u);
   }
   uint32_t tot;
-  const uint32_t p_eq = block_scan<THREADS>(eq, wsum, &tot);
+  const uint32_t ex = block_scan<THREADS>((gt << 16) | eq, wsum, &tot);
+  const uint32_t p_gt = ex >> 16, p_eq = ex & 0xffffu;
+  uint32_t o = p_gt + min(p_eq, need_eq);
   const uint32_t take = need_eq > p_eq ? min(need_eq - p_eq, eq) : 0u;
-  uint32_t n_sel;
-  uint32_t o = block_scan<THREADS>(gt + take, wsum, &n_sel);
+  const uint32_t n_sel = (tot >> 16) + min(tot & 0xffffu, need_eq);
   uint32_t taken = 0;
   const int64_t obase = FINAL ? int64_t(row) * a.k : (int64_t(row) * a.nchunks + chunk) * a.k;
 #pragma unroll
   for (int t = 0; t < ITEMS; ++t) {
-    const uint32_t key = keys[j0 + t];
-    bool sel = key > thr;
-    if (!sel && key == thr && key != 0u && taken < take) { sel = true; ++taken; }
+    const uint32_t kk = key[t];
+    bool sel = kk > thr;
+    if (!sel && kk == thr && kk != 0u && taken < take) { sel = true; ++taken; }
     if (sel) {
-      const int index = FROM_CAND ? idxs[j0 + t] : int(base + j0 + t);
+      int index;
+      if constexpr (FROM_CAND) index = kidx[t];
+      else index = int(base + j0 + t);
       if constexpr (FINAL) {
         a.out_idx[obase + o] = index;
       } else {
-        a.okey[obase + o] = key;
+        a.okey[obase + o] = kk;
         a.oidx[obase + o] = index;
       }
       ++o;
@@ -174,30 +329,53 @@ __global__ __launch_bounds__(THREADS) void topk_select(SelectArgs a) {
   }
 }
 
+// Launch one selection level.  `tile` is the number of positions one
+// workgroup stages (THREADS*ITEMS of the chosen instance).
 template <bool FROM_CAND, bool FINAL>
-void launch_select(const SelectArgs& a, int len, int R, int nchunks, hipStream_t s) {
+void launch_select(const SelectArgs& a, int tile, int R, int nchunks, hipStream_t s) {
   const dim3 grid(R, nchunks);
-  if (len <= 2048 && !FROM_CAND && nchunks == 1)
+  if (tile == 2048)
     hipLaunchKernelGGL((topk_select<256, 8, FROM_CAND, FINAL>), grid, dim3(256), 0, s, a);
-  else if (len <= 8192 && nchunks == 1)
+  else if (tile == 8192)
     hipLaunchKernelGGL((topk_select<512, 16, FROM_CAND, FINAL>), grid, dim3(512), 0, s, a);
   else
     hipLaunchKernelGGL((topk_select<1024, 16, FROM_CAND, FINAL>), grid, dim3(1024), 0, s, a);
 }
 
-int64_t chunks_of(int64_t len) { return (len + kMaxTile - 1) / kMaxTile; }
+int tile_for(int64_t len) { return len <= 2048 ? 2048 : (len <= 8192 ? 8192 : kMaxTile); }
+
+// Levels: the first cuts raw rows into chunks of `first` positions (small
+// chunks when there are few rows, so that many workgroups share a row); the
+// following ones reduce candidate lists in kMaxTile chunks; the last one
+// selects from at most kMaxTile positions.
+struct Levels {
+  int n;
+  int64_t len[8];    // positions per row entering level i
+  int tile[8];       // positions per workgroup at level i
+  int64_t cand_max;  // largest candidate list per row
+};
+
+Levels levels_of(int R, int N, int k) {
+  Levels L{};
+  int64_t len = N;
+  const int first = kMaxTile;
+  while (true) {
+    const int tile = L.n == 0 ? (len > first ? first : tile_for(len)) : (len > kMaxTile ? kMaxTile : tile_for(len));
+    L.len[L.n] = len;
+    L.tile[L.n] = tile;
+    ++L.n;
+    if (len <= tile) break;
+    len = (len + tile - 1) / tile * k;
+    L.cand_max = std::max(L.cand_max, len);
+  }
+  return L;
+}
 
 }  // namespace
 
 TopkPlan plan_topk(int R, int N, int k) {
-  TopkPlan p{0, 0, 0};
-  int64_t len = N, maxlen = 0;
-  while (len > kMaxTile) {
-    len = chunks_of(len) * k;
-    maxlen = std::max(maxlen, len);
-    ++p.levels;
-  }
-  p.cand_elems = int64_t(R) * maxlen;
+  const Levels L = levels_of(R, N, k);
+  TopkPlan p{L.n - 1, int64_t(R) * L.cand_max, 0};
   p.ws_bytes = p.levels ? size_t(2) * size_t(p.cand_elems) * (sizeof(uint32_t) + sizeof(int)) : 0;
   return p;
 }
@@ -205,60 +383,49 @@ TopkPlan plan_topk(int R, int N, int k) {
 hipError_t launch_topk(const float* scores, const int* n_valid, int R, int N, int k, int* idx, void* ws,
                        hipStream_t stream) {
   if (R == 0) return hipSuccess;
+  const Levels L = levels_of(R, N, k);
   const TopkPlan plan = plan_topk(R, N, k);
-  SelectArgs a{};
-  a.scores = scores;
-  a.n_valid = n_valid;
-  a.k = k;
-  a.out_idx = idx;
-  if (plan.levels == 0) {
-    a.in_len = N;
-    a.nchunks = 1;
-    launch_select<false, true>(a, N, R, 1, stream);
-    return hipGetLastError();
+  uint32_t* key_buf[2] = {nullptr, nullptr};
+  int* idx_buf[2] = {nullptr, nullptr};
+  if (plan.levels) {
+    char* w = static_cast<char*>(ws);
+    for (int i = 0; i < 2; ++i) {
+      key_buf[i] = reinterpret_cast<uint32_t*>(w);
+      w += plan.cand_elems * sizeof(uint32_t);
+      idx_buf[i] = reinterpret_cast<int*>(w);
+      w += plan.cand_elems * sizeof(int);
+    }
   }
-  uint32_t* key_buf[2];
-  int* idx_buf[2];
-  char* w = static_cast<char*>(ws);
-  for (int i = 0; i < 2; ++i) {
-    key_buf[i] = reinterpret_cast<uint32_t*>(w);
-    w += plan.cand_elems * sizeof(uint32_t);
-    idx_buf[i] = reinterpret_cast<int*>(w);
-    w += plan.cand_elems * sizeof(int);
+  int cur = -1;  // -1: the raw score rows
+  for (int l = 0; l < L.n; ++l) {
+    const bool last = l == L.n - 1;
+    const int64_t len = L.len[l];
+    const int tile = L.tile[l];
+    const int nch = last ? 1 : int((len + tile - 1) / tile);
+    SelectArgs a{};
+    a.k = k;
+    a.in_len = int(len);
+    a.nchunks = nch;
+    if (cur < 0) {
+      a.scores = scores;
+      a.n_valid = n_valid;
+    } else {
+      a.ckey = key_buf[cur];
+      a.cidx = idx_buf[cur];
+    }
+    if (last) {
+      a.out_idx = idx;
+      if (cur < 0) launch_select<false, true>(a, tile, R, 1, stream);
+      else launch_select<true, true>(a, tile, R, 1, stream);
+    } else {
+      const int nxt = cur < 0 ? 0 : cur ^ 1;
+      a.okey = key_buf[nxt];
+      a.oidx = idx_buf[nxt];
+      if (cur < 0) launch_select<false, false>(a, tile, R, nch, stream);
+      else launch_select<true, false>(a, tile, R, nch, stream);
+      cur = nxt;
+    }
   }
-  // level 1: raw scores -> per-chunk candidates
-  int64_t len = N;
-  int nch = int(chunks_of(len));
-  a.in_len = N;
-  a.nchunks = nch;
-  a.okey = key_buf[0];
-  a.oidx = idx_buf[0];
-  launch_select<false, false>(a, N, R, nch, stream);
-  len = int64_t(nch) * k;
-  int cur = 0;
-  // further levels: candidates -> candidates
-  while (len > kMaxTile) {
-    nch = int(chunks_of(len));
-    SelectArgs c{};
-    c.ckey = key_buf[cur];
-    c.cidx = idx_buf[cur];
-    c.in_len = int(len);
-    c.k = k;
-    c.nchunks = nch;
-    c.okey = key_buf[cur ^ 1];
-    c.oidx = idx_buf[cur ^ 1];
-    launch_select<true, false>(c, int(len), R, nch, stream);
-    cur ^= 1;
-    len = int64_t(nch) * k;
-  }
-  SelectArgs f{};
-  f.ckey = key_buf[cur];
-  f.cidx = idx_buf[cur];
-  f.in_len = int(len);
-  f.k = k;
-  f.nchunks = 1;
-  f.out_idx = idx;
-  launch_select<true, true>(f, int(len), R, 1, stream);
   return hipGetLastError();
 }
 
