@@ -84,11 +84,16 @@ def _f32(x, device):
 class DecodeWorkload:
     """One decode step for B sequences (CSA or HCA) on rotated cache copies."""
 
-    def __init__(self, cfg, device, copies=COPIES):
+    def __init__(self, cfg, device, copies=COPIES, batch=None):
         import torch
+        lengths = synth.decode_lengths(cfg)
+        if batch is not None:  # the first `batch` sequences of the workload's draw
+            import dataclasses
+            cfg = dataclasses.replace(cfg, B=batch)
+            lengths = lengths[:batch]
         self.cfg, self.device = cfg, device
         B, D, DI = cfg.B, cfg.D, cfg.D_I
-        self.lengths = synth.decode_lengths(cfg)
+        self.lengths = lengths
         self.Ncap = synth.decode_capacity(cfg)
         self.R = synth.staging_rows(cfg)
         self.seqs = [synth.decode_seq(cfg, b, self.lengths) for b in range(B)]

@@ -6,5 +6,5 @@ with the HIP library and imports nothing from it.
 """
 from . import csa, pipeline  # noqa: F401
 from .csa import (NEG_INF, attend, compress, compress_entry, entry_candidates, entry_from_rows, hca_attn,  # noqa: F401
-                  index_score, pool, rms_norm, rope, sparse_attn, topk, visible,
+                  index_score, pool, rms_norm, rope, round_bf16, sparse_attn, topk, visible,
                   window_positions, StreamingCompressor)

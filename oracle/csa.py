@@ -77,6 +77,23 @@ def rope(x, pos, rope_dim, base=10000.0, inverse=False):
     return x
 
 
+def round_bf16(x):
+    """Value of x after storage as bfloat16 (round to nearest, ties to even).
+
+    The compressed caches of the bf16 workloads are stored as bfloat16: the
+    8 exponent bits of float32 and its top 7 fraction bits.  x is first
+    rounded to float32 (nearest even), then the low 16 bits of that float32
+    are rounded away (nearest even).  Finite inputs only.
+    """
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    low = u & 0xFFFF
+    keep = u >> 16
+    up = (low > 0x8000) | ((low == 0x8000) & ((keep & 1) == 1))
+    keep = (keep + up.astype(np.uint64)) & 0xFFFF
+    return (keep.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
 def rms_norm(y, gamma, eps):
     """RMSNorm over the last axis, ``y / sqrt(mean(y^2) + eps) * gamma``.
 

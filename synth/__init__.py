@@ -103,9 +103,9 @@ def gaussian(rng, shape):
 
 def unit_rms(rng, shape):
     """Gaussian rows scaled to unit RMS along the last axis (float32)."""
-    x = rng.standard_normal(shape, dtype=np.float64)
-    x /= np.sqrt(np.mean(x * x, axis=-1, keepdims=True))
-    return x.astype(np.float32)
+    x = rng.standard_normal(shape, dtype=np.float32)
+    x *= 1.0 / np.sqrt(np.mean(np.square(x, dtype=np.float64), axis=-1, keepdims=True)).astype(np.float32)
+    return x
 
 
 def cache_rows(cid, tid, b, rows, d, lo=0):
@@ -121,6 +121,17 @@ def cache_rows(cid, tid, b, rows, d, lo=0):
         blk = bf16_bits(unit_rms(stream(cid, tid, b, c), (CHUNK_ROWS, d)))
         s0, s1 = max(a, lo), z
         out[s0 - lo:s1 - lo] = blk[s0 - a:s1 - a]
+    return out
+
+
+def cache_rows_at(cid, tid, b, index, d):
+    """Rows at the given indices of the same cache (each chunk drawn once)."""
+    index = np.asarray(index, dtype=np.int64)
+    out = np.empty((index.size, d), dtype=np.uint16)
+    for c in np.unique(index // CHUNK_ROWS):
+        blk = bf16_bits(unit_rms(stream(cid, tid, b, int(c)), (CHUNK_ROWS, d)))
+        sel = np.nonzero(index // CHUNK_ROWS == c)[0]
+        out[sel] = blk[index[sel] - c * CHUNK_ROWS]
     return out
 
 
@@ -237,6 +248,11 @@ def decode_shared(cfg):
 def kv_cache_rows(cfg, b, rows, lo=0):
     """Pre-filled compressed KV cache rows [lo, rows) of sequence b (bf16 bits)."""
     return cache_rows(cfg.cid, T_KVCACHE, b, rows, cfg.D, lo)
+
+
+def kv_cache_rows_at(cfg, b, index):
+    """Pre-filled compressed KV cache rows at the given indices of sequence b."""
+    return cache_rows_at(cfg.cid, T_KVCACHE, b, index, cfg.D)
 
 
 def idx_cache_rows(cfg, b, rows, lo=0):

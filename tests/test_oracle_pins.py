@@ -6,6 +6,7 @@ import math
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 from oracle import csa
@@ -157,3 +158,26 @@ def test_rope_large_position_angle_in_float64():
     y = oracle.rope(x, 1048575, 64)
     assert y[0] == pytest.approx(math.cos(1048575.0), abs=1e-12)
     assert y[1] == pytest.approx(math.sin(1048575.0), abs=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# bfloat16 storage rounding
+# ---------------------------------------------------------------------------
+def test_round_bf16_known_values():
+    one = 1.0
+    ulp = 2.0 ** -7                      # bf16 spacing in [1, 2)
+    assert oracle.round_bf16(one) == one
+    assert oracle.round_bf16(one + ulp / 2) == one                 # tie -> even (1.0)
+    assert oracle.round_bf16(one + 3 * ulp / 2) == one + 2 * ulp   # tie -> even (1 + 2 ulp)
+    assert oracle.round_bf16(one + ulp * 0.51) == one + ulp
+    assert oracle.round_bf16(-3.0) == -3.0
+    assert oracle.round_bf16(0.0) == 0.0
+
+
+def test_round_bf16_matches_torch_conversion():
+    """Library routine: torch's float32 -> bfloat16 conversion (nearest even)."""
+    rng = np.random.default_rng(21)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-6, 6, 20000),
+                        np.float32(1.0) + np.arange(-300, 300) * np.float32(2.0 ** -16)]).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(oracle.round_bf16(x), want)
