@@ -510,16 +510,45 @@ def measure(wl, steps, warmup, only=None):
     return res
 
 
+KERNEL_SOURCE = {"index_score": "index_score.hip", "topk": "topk.hip", "sparse_attn": "attn.hip",
+                 "hca_attn": "attn.hip", "compress_kv": "compress.hip", "compress_idx": "compress.hip"}
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary of this workload (profiles/*_<workload>.md: FETCH_SIZE and
+    WRITE_SIZE scaled by a plain copy), or None when there is none or the
+    kernel source has changed since the counters were taken."""
+    import glob
+    import hashlib
+    csrc = os.path.join(ROOT, "compressed_sparse_attention_06_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCE[kernel], "common.h", "kernels.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    for path in glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}.md")):
+        fields = {}
+        with open(path) as fh:
+            for line in fh:
+                if ":" in line and line.split(":", 1)[0] in ("traffic_kernel", "traffic_bytes_per_launch",
+                                                              "source_sha256"):
+                    k, v = line.split(":", 1)
+                    fields[k] = v.strip()
+        if fields.get("traffic_kernel") == kernel and fields.get("source_sha256") == h.hexdigest():
+            return int(float(fields["traffic_bytes_per_launch"]))
+    return None
+
+
 def roofline(wl, m):
     dom, t = m["dom"], m["dom_ms"] * 1e-3
     if isinstance(wl, PrefillWorkload):
         ach = m["fl"][dom] / t / 1e12
         return dict(bound="mfma", achieved=round(ach, 2), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(ach / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None, kernel=dom,
+                    frac=round(ach / MFMA_BF16_PEAK_TFLOPS, 4), traffic=measured_traffic(wl.cfg.name, dom), kernel=dom,
                     kernel_us=round(m["dom_ms"] * 1e3, 2), algorithmic_flops=m["fl"][dom], per_unit=wl.unit())
     ach = m["by"][dom] / t / 1e9
     return dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4),
-                traffic=None, kernel=dom, kernel_us=round(m["dom_ms"] * 1e3, 2), algorithmic_bytes=m["by"][dom],
+                traffic=measured_traffic(wl.cfg.name, dom), kernel=dom, kernel_us=round(m["dom_ms"] * 1e3, 2), algorithmic_bytes=m["by"][dom],
                 per_unit=wl.unit())
 
 
