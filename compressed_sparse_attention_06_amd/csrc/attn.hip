@@ -35,6 +35,12 @@ constexpr int kH = 64;      // heads on the matrix-core path
 constexpr int kD = 512;     // K=V row width on the matrix-core path
 constexpr int kTile = 32;   // candidate rows per tile
 constexpr int kKPitch = kD + 8;     // bf16 elements per K row in LDS (16 B pad)
+// K tile in LDS: 16-byte chunk c of row r sits at chunk c ^ (4 * ((r >> 4) & 1)).
+// With the 16-byte row pad, the 16 rows one S^T fragment reads then start on
+// 16 different bank groups, so its 64 lanes spread evenly over the banks.
+__device__ __forceinline__ int kt_off(int row, int chunk) {
+  return row * kKPitch + ((chunk ^ (((row >> 4) & 1) << 2)) << 3);
+}
 // V^T in LDS: row d (one dim, 32 candidate rows) starts at d*32 + (d/8)*8
 // elements; the 16-byte skew per 8 dims spreads the transposed tile writes
 // (lanes 8 dims apart) over all LDS banks.
@@ -173,7 +179,7 @@ __global__ __launch_bounds__(256) void attn_mfma(AttnArgs a, int nsplit, int chu
   for (int jl0 = 0; jl0 < n_rows; jl0 += kTile) {
 #pragma unroll
     for (int r = 0; r < 8; ++r)
-      *reinterpret_cast<uint4*>(&Kt[(rg * 8 + r) * kKPitch + dc * 8]) = v[r];
+      *reinterpret_cast<uint4*>(&Kt[kt_off(rg * 8 + r, dc)]) = v[r];
     // transpose the 8x8 block: Vt[dim][rows rg*8 .. +7]
 #pragma unroll
     for (int dd = 0; dd < 8; ++dd) {
@@ -201,11 +207,10 @@ __global__ __launch_bounds__(256) void attn_mfma(AttnArgs a, int nsplit, int chu
     for (int t = 0; t < 2; ++t) {
       const int arow = (r16 / 4) * 8 + t * 4 + (r16 % 4);
       floatx4 st = floatx4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* kr = &Kt[arow * kKPitch + g * 8];
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks)
-        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(*reinterpret_cast<const uint4*>(kr + ks * 32)),
-                                                     qb[ks], st, 0, 0, 0);
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            as_bf16x8(*reinterpret_cast<const uint4*>(&Kt[kt_off(arow, ks * 4 + g)])), qb[ks], st, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) s8[t * 4 + i] = st[i];
     }

@@ -14,9 +14,10 @@
 //    from HBM into registers (every load instruction covers 64 contiguous
 //    bytes of 16 rows), 4 x 16x16x32 MFMA per 16 rows and K-step, then ReLU,
 //    head weights and a two-step cross-lane sum.
-//  * index_tile (many queries, e.g. prefill): a workgroup keeps a tile of
-//    index rows stationary in registers and streams query operands through
-//    LDS; causal tiles that no query of the block can see are skipped.
+//  * index_tile (many queries per sequence, e.g. prefill): a workgroup stages
+//    512 index rows in LDS once; each wave then scores its own queries
+//    against them without further barriers, stopping at each query's causal
+//    bound.
 //
 // A and B share the K order of a K-step: lane group g, element i <-> dim
 // ks*32 + g*8 + i.
@@ -46,7 +47,7 @@ constexpr int kStepRows = kStreamWaves * 64;
 
 template <int STEPS>
 __global__ __launch_bounds__(kWave* kStreamWaves) void index_stream(IndexArgs a) {
-  __shared__ uint4 qs[kHI * kDI / 8];
+  __shared__ uint4 qs[kHI * (kDI / 8 + 1)];
   __shared__ float wsh[kHI];
   const int64_t qi = blockIdx.x;
   const int b = int(qi / a.S);
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(kWave* kStreamWaves) void index_stream(IndexArgs a)
   load(0, kb0);
   {
     const uint4* q = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q_idx) + qi * (kHI * kDI));
-    for (int i = tid; i < kHI * kDI / 8; i += kWave * kStreamWaves) qs[i] = q[i];
+    for (int i = tid; i < kHI * kDI / 8; i += kWave * kStreamWaves) qs[(i / (kDI / 8)) * (kDI / 8 + 1) + i % (kDI / 8)] = q[i];
     if (tid < kHI) wsh[tid] = a.w[qi * kHI + tid];
   }
   __syncthreads();
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(kWave* kStreamWaves) void index_stream(IndexArgs a)
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qa[mt][ks] = as_bf16x8(qs[(mt * 16 + r16) * (kDI / 8) + ks * 4 + g]);
+    for (int ks = 0; ks < 4; ++ks) qa[mt][ks] = as_bf16x8(qs[(mt * 16 + r16) * (kDI / 8 + 1) + ks * 4 + g]);
   float wv[4][4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -143,6 +144,128 @@ __global__ __launch_bounds__(kWave* kStreamWaves) void index_stream(IndexArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// Tile kernel (many queries per sequence, e.g. prefill): grid 1-D, 8 waves.
+// A block owns 32 queries x 512 index rows.  The rows are staged once into
+// LDS (row pitch padded by 16 bytes so that the 16 rows of a fragment sit on
+// different banks); after that single barrier every wave runs on its own:
+// it holds one query's 64x128 operand in VGPRs (the next query's operand in
+// flight), streams 16-row tiles of the block's rows from LDS as MFMA B
+// operands, and stops at the query's causal bound.  The entry tiles of one
+// query chunk go to one XCD back to back (workgroups are dealt round-robin
+// over the 8 XCDs), so a chunk's query operands come from HBM once and then
+// from that XCD's L2.
+// ---------------------------------------------------------------------------
+constexpr int kTileQ = 32;
+constexpr int kTileE = 512;
+constexpr int kXcd = 8;
+constexpr int kRowVec = kDI / 8;      // uint4 per index row
+constexpr int kRowPitch = kRowVec + 1;
+
+constexpr int kNT = 2;  // 16-row tiles per MFMA step of the tile kernel
+
+__global__ __launch_bounds__(kWave* kStreamWaves) void index_tile(IndexArgs a, int qchunks_per_seq, int etiles,
+                                                                 int nchunks) {
+  __shared__ uint4 rows[kTileE * kRowPitch];
+  __shared__ float wsh[kTileQ][kHI];
+  __shared__ int svis[kTileQ];
+  constexpr int kThreads = kWave * kStreamWaves;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int g = lane / 16, r16 = lane % 16;
+  const int xcd = blockIdx.x % kXcd, local = blockIdx.x / kXcd;
+  const int chunk = (local / etiles) * kXcd + xcd;
+  const int tile = local % etiles;
+  if (chunk >= nchunks) return;
+  const int b = chunk / qchunks_per_seq;
+  const int s0 = (chunk % qchunks_per_seq) * kTileQ;
+  const int nq = min(kTileQ, a.S - s0);
+  const int64_t q0 = int64_t(b) * a.S + s0;
+  const int Ncap = a.Ncap;
+  const int e_blk = tile * kTileE;
+  const int e_end = min(e_blk + kTileE, Ncap);
+  if (tid < kTileQ) svis[tid] = tid < nq ? int(visible_entries(a.pos, q0 + tid, a.ratio, Ncap)) : 0;
+  __syncthreads();
+  int vmax = 0;
+  for (int j = 0; j < nq; ++j) vmax = max(vmax, svis[j]);
+  if (e_blk >= vmax) {  // no query of the chunk sees any row of the tile
+    for (int j = 0; j < nq; ++j)
+      for (int e = e_blk + tid; e < e_end; e += kThreads) a.scores[(q0 + j) * Ncap + e] = -INFINITY;
+    return;
+  }
+  // stage the visible part of the block's rows
+  {
+    const int n_rows = min(e_end, vmax) - e_blk;
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.cache) +
+                                                      (int64_t(b) * Ncap + e_blk) * kDI);
+    for (int i = tid; i < n_rows * kRowVec; i += kThreads) rows[(i / kRowVec) * kRowPitch + i % kRowVec] = src[i];
+    for (int i = tid; i < nq * kHI; i += kThreads) wsh[i / kHI][i % kHI] = a.w[q0 * kHI + i];
+  }
+  __syncthreads();
+
+  const uint4* qsrc = reinterpret_cast<const uint4*>(a.q_idx);
+  auto fetch = [&](int j, bf16x8 (&dst)[4][4]) {
+    const uint4* q = qsrc + (q0 + j) * (kHI * kRowVec);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) dst[mt][ks] = as_bf16x8(q[(mt * 16 + r16) * kRowVec + ks * 4 + g]);
+  };
+  auto score_query = [&](int j, const bf16x8 (&qa)[4][4]) {
+    const float* wq = wsh[j] + g * 4;
+    const int nv = svis[j];
+    float* srow = a.scores + (q0 + j) * Ncap;
+    const int e_vis = min(e_end, nv);  // rows [e_blk, e_vis) are scored, the rest of the tile is -inf
+    for (int e = max(e_vis, e_blk) + lane; e < e_end; e += kWave) srow[e] = -INFINITY;
+    // kNT 16-row tiles (4*kNT independent accumulator chains) per step keep
+    // the matrix pipe fed; the ReLU / weight epilogue follows each step
+    for (int t0 = e_blk; t0 < e_vis; t0 += kNT * 16) {
+      floatx4 acc[kNT][4];  // [16-row tile][head tile]
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+          const bf16x8 kk = as_bf16x8(rows[(t0 - e_blk + nt * 16 + r16) * kRowPitch + g + ks * 4]);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+            acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][ks], kk, acc[nt][mt], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) {
+        float part = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const float4 w4 = *reinterpret_cast<const float4*>(wq + mt * 16);
+          part += fmaxf(acc[nt][mt][0], 0.f) * w4.x + fmaxf(acc[nt][mt][1], 0.f) * w4.y +
+                  fmaxf(acc[nt][mt][2], 0.f) * w4.z + fmaxf(acc[nt][mt][3], 0.f) * w4.w;
+        }
+        part += __shfl_xor(part, 16, kWave);
+        part += __shfl_xor(part, 32, kWave);
+        const int e = t0 + nt * 16 + r16;
+        if (g == 0 && e < e_end) srow[e] = e < nv ? part : -INFINITY;
+      }
+    }
+  };
+  // wave w takes queries w, w+8, ...; two operand sets alternate so that the
+  // next query's operand is in flight while the current one is scored
+  bf16x8 qa0[4][4], qa1[4][4];
+  int j = wave;
+  if (j < nq) fetch(j, qa0);
+  while (j < nq) {
+    if (j + kStreamWaves < nq) fetch(j + kStreamWaves, qa1);
+    score_query(j, qa0);
+    j += kStreamWaves;
+    if (j >= nq) break;
+    if (j + kStreamWaves < nq) fetch(j + kStreamWaves, qa0);
+    score_query(j, qa1);
+    j += kStreamWaves;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Vector-ALU kernel for other shapes / fp32: one thread per (query, entry).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void index_any(IndexArgs a) {
@@ -174,7 +297,14 @@ __global__ __launch_bounds__(256) void index_any(IndexArgs a) {
 hipError_t launch_index_score(const IndexArgs& a, hipStream_t stream) {
   const int64_t nq = int64_t(a.B) * a.S;
   if (nq == 0 || a.Ncap == 0) return hipSuccess;
-  if (a.use_mfma && a.H == kHI && a.D == kDI) {
+  if (a.use_mfma && a.H == kHI && a.D == kDI && a.S >= 2 * kTileQ) {
+    const int qcs = (a.S + kTileQ - 1) / kTileQ;
+    const int nchunks = a.B * qcs;
+    const int etiles = (a.Ncap + kTileE - 1) / kTileE;
+    const int64_t nblocks = int64_t((nchunks + kXcd - 1) / kXcd) * kXcd * etiles;
+    hipLaunchKernelGGL(index_tile, dim3(unsigned(nblocks)), dim3(kWave * kStreamWaves), 0, stream, a, qcs, etiles,
+                       nchunks);
+  } else if (a.use_mfma && a.H == kHI && a.D == kDI) {
     const int64_t blocks1 = nq * ((a.Ncap + kStepRows - 1) / kStepRows);
     if (blocks1 <= 4096) {
       const dim3 grid(unsigned(nq), (a.Ncap + kStepRows - 1) / kStepRows);

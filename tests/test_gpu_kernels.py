@@ -134,6 +134,26 @@ def test_index_score(H, D, dtype):
         assert_normwise(got[b], want, what=f"b={b}")
 
 
+def test_index_score_tile_path():
+    """Many queries per sequence (the prefill kernel): ragged query chunks and
+    entry tiles, causal and capped visibility, queries with nothing visible."""
+    csa = csa_mod()
+    B, S, H, D, Ncap, r = 2, 100, 64, 128, 1100, 4
+    pos = np.stack([np.arange(S, dtype=np.int32) * 37 - 5, np.arange(S, dtype=np.int32) + 4390]).astype(np.int32)
+    q = rows_bf16(24, (B, S, H, D), unit=True)
+    k = rows_bf16(25, (B, Ncap, D), unit=True)
+    w = (np.random.default_rng(26).standard_normal((B, S, H)) / math.sqrt(D) / math.sqrt(H)).astype(np.float32)
+    scores = torch.empty((B, S, Ncap), device="cuda")
+    csa.csa_index_score(dev_bf16(q), dev(w), dev_bf16(k), dev(pos), scores, ratio=r)
+    got = scores.cpu().numpy()
+    for b in range(B):
+        kb = synth.bf16_to_f64(k[b])
+        want = np.stack([oracle.index_score(synth.bf16_to_f64(q[b, s]), w[b, s], kb,
+                                            oracle.visible(int(pos[b, s]), r) if pos[b, s] >= 0 else 0)
+                         for s in range(S)])
+        assert_normwise(got[b], want, what=f"b={b}")
+
+
 # ---------------------------------------------------------------------------
 # Top-k (identical float32 scores on both sides: bit-exact sets)
 # ---------------------------------------------------------------------------
