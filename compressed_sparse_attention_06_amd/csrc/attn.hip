@@ -10,21 +10,33 @@
 // section "3 Giải pháp" (all query heads share one K/V head).
 //
 // Matrix-core path (bf16, 64 heads, D = 512).  All 64 heads of a query share
-// every K=V row, so one workgroup (4 waves x 16 heads) gathers each 32-row
-// candidate tile once into LDS -- row-major for the QK product and transposed
-// for the PV product -- and runs both products on 16x16x32 bf16 MFMA:
-//   S^T[rows x heads] = K . Q^T   (A = K rows from LDS, B = Q held in VGPRs)
-//   O^T[dims x heads] += V^T . P^T (A = V^T from LDS, B = P straight from the
-//                                  S^T accumulators, no shuffle)
-// The tile's A rows are permuted so that each lane's eight S^T results are
-// eight consecutive candidate rows, exactly the K-slice its P^T operand
-// needs.  Softmax state (running max, partial sums) is per head = per lane,
-// so the rescale of the 128 output accumulators is lane-local.
+// every K=V row.  A workgroup of eight waves (two per SIMD) takes one query,
+// or one split of its candidate list, in tiles of 32 candidate rows, with the
+// waves specialised:
+//   * QK waves 0..3: wave w holds Q^T of heads 32*(w&1)..+32 in VGPRs and
+//     scores rows 16*(w>>1)..+16 of each tile on 16x16x32 bf16 MFMA
+//     (S^T = K . Q^T), then writes P = exp2(S - m) to LDS as bf16;
+//   * PV waves 4..7: wave 4+v owns O^T for dims 128v..+128 and all 64 heads
+//     and accumulates O^T += V^T . P^T one tile behind the QK waves; its V^T
+//     operand comes from the row-major tile through the transposing LDS read
+//     (ds_read_b64_tr_b16).
+// On each SIMD one QK and one PV wave share the matrix core, so the softmax
+// arithmetic of one overlaps the products of the other.  Tile rows are copied
+// HBM -> LDS by the load unit itself (one 1 KiB row per wave instruction),
+// two tiles ahead, into a ring of four tile buffers; one barrier per tile
+// step orders everything.
+//
+// Softmax reference: every head accumulates exp2(s - m) against a fixed
+// reference m = its sink logit (log2 units), so no maxima are exchanged and
+// O is never rescaled; fp32 accumulators and bf16 P hold values up to 2^64
+// times the reference with room to spare.  Should a score exceed the
+// reference by more than that headroom, the whole pass is repeated with the
+// true maximum as the reference (never for ordinary data).
 //
 // Few queries (decode) split the candidate list over workgroups; each writes
-// an unnormalised partial (O, max, sum) and a combine kernel merges the
-// splits with the sink and applies the inverse RoPE.  With one split the sink
-// seeds the running max/sum and the kernel finishes the output itself.
+// an unnormalised partial (O, m, sum) and a combine kernel merges the splits
+// with the sink and applies the inverse RoPE.  With one split the sink's
+// unit term is part of the sum and the kernel finishes the output itself.
 #include "common.h"
 #include "kernels.h"
 
@@ -33,23 +45,63 @@ namespace {
 
 constexpr int kH = 64;      // heads on the matrix-core path
 constexpr int kD = 512;     // K=V row width on the matrix-core path
-constexpr int kTile = 32;   // candidate rows per tile
-constexpr int kKPitch = kD + 8;     // bf16 elements per K row in LDS (16 B pad)
-// K tile in LDS: 16-byte chunk c of row r sits at chunk c ^ (4 * ((r >> 4) & 1)).
-// With the 16-byte row pad, the 16 rows one S^T fragment reads then start on
-// 16 different bank groups, so its 64 lanes spread evenly over the banks.
-__device__ __forceinline__ int kt_off(int row, int chunk) {
-  return row * kKPitch + ((chunk ^ (((row >> 4) & 1) << 2)) << 3);
-}
-// V^T in LDS: row d (one dim, 32 candidate rows) starts at d*32 + (d/8)*8
-// elements; the 16-byte skew per 8 dims spreads the transposed tile writes
-// (lanes 8 dims apart) over all LDS banks.
-__device__ __forceinline__ int vt_off(int d) { return d * kTile + (d >> 3) * 8; }
-constexpr int kVtElems = kD * kTile + (kD / 8) * 8;
+constexpr int kT = 32;      // candidate rows per tile
+constexpr int kBufs = 4;    // tile ring: PV tile, QK tile, two copies in flight
+constexpr int kWaves = 8;   // 4 QK + 4 PV waves
+constexpr int kThreads = kWaves * kWave;
+constexpr int kCopyRows = kT / kWaves;  // rows each wave copies per tile
+constexpr int kRowBytes = kD * 2;
+// LDS row pitch 1 KiB + 32 B (consecutive rows start 8 banks apart) and, in
+// rows with bit 2 set, the two 16-byte chunks of each 32-byte pair swapped.
+// Then the 8 rows one 128-bit K read serves per cycle, and the 4 rows x 2
+// chunks one transposing V read serves per cycle, all fall on distinct banks,
+// while every per-step offset stays an immediate.
+constexpr int kPitch = kRowBytes + 32;
+__device__ __forceinline__ int row_swap(int r) { return (r >> 2) & 1; }
+constexpr int kPPitch = kT + 8;   // bf16 per head row of P in LDS (80 B: 8 heads on distinct banks)
+constexpr int kAheadK = 4;        // K operand prefetch distance, in K-steps
+constexpr int kAheadV = 3;        // V^T operand prefetch distance, in dim tiles
+constexpr float kHeadroom = 64.f;  // log2 of the largest P relative to the reference
 constexpr int kMinSplitRows = 64;
+constexpr int kSplitGrain = 32;
 constexpr int kTargetBlocks = 256;
-constexpr int kMaxChunk = 4352;   // CSA candidates of one block, resolved in LDS
+constexpr int kMaxChunk = 1024;   // CSA candidates of one block, resolved in LDS
 constexpr int kMaxSplits = 256;
+
+// One 1 KiB row copy HBM -> LDS through the load unit: lane l moves the 16
+// bytes at row + voff to LDS address lds_row + 16 l (M0 carries lds_row).
+// Written as asm so that the compiler does not order LDS reads of other tile
+// buffers behind it; the kernel waits for these copies itself before the
+// barrier that publishes a tile.
+__device__ __forceinline__ void copy_row_to_lds(const void* row, uint32_t voff, uint32_t lds_row) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(row), "{m0}"(lds_row) : "memory");
+}
+// s_waitcnt with only the vector-memory count set (expcnt, lgkmcnt: no wait)
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 4 x 16-bit transposing LDS read: within each 16-lane group, lane j gets
+// element j%4 of the 8-byte chunks addressed by lanes 4i + j/4 (i = 0..3).
+__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
+  const shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p));
+  uint2 r;
+  __builtin_memcpy(&r, &v, 8);
+  return r;
+}
+
+// Finite reference of a head: its sink logit in log2 units (0 if the sink is
+// not finite; a -inf sink then contributes exp2(-inf) = 0 to the sum).
+__device__ __forceinline__ float sink_ref(const float* sink, int h) {
+  const float s2 = sink[h] * kLog2e;
+  return (s2 > -1e30f && s2 < 1e30f) ? s2 : 0.f;
+}
 
 struct Cand {
   int n_win;
@@ -105,197 +157,263 @@ __device__ __forceinline__ int cand_code(const AttnArgs& a, bool hca, const Cand
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core kernel: grid (B*S, nsplit), 256 threads.
+// Matrix-core kernel: grid (B*S, nsplit), 512 threads (8 waves), one
+// workgroup per CU.
 // ---------------------------------------------------------------------------
 template <bool HCA, bool SPLIT>
-__global__ __launch_bounds__(256) void attn_mfma(AttnArgs a, int nsplit, int chunk_rows) {
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[kTile * kKPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[kVtElems];
-  __shared__ float rope_cs[kD];
-  __shared__ unsigned char valid[kTile];
+__global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, int chunk_rows) {
+  __shared__ __attribute__((aligned(16))) unsigned char tiles[kBufs][kT * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t pt[2][kH * kPPitch];
+  __shared__ __attribute__((aligned(4))) uint8_t vmask[kBufs][kWaves];
+  __shared__ float lsum[2][kH];
+  __shared__ float mseen[2][kH];
+  __shared__ float mref[kH];  // reference of the current pass, per head
+  __shared__ int over_flag;
   __shared__ int codes[HCA ? 1 : kMaxChunk];
 
   const int64_t qi = blockIdx.x;
   const int split = blockIdx.y;
   const int b = int(qi / a.S);
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int g = lane / 16, r16 = lane % 16;
-  const int head = wave * 16 + r16;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int g = lane / 16, c16 = lane % 16;
   const Cand c = candidates(a, HCA, qi);
   const int64_t n_cand = c.n_win + c.n_sel;
   const int64_t j_begin = int64_t(split) * chunk_rows;
   const int n_rows = int(j_begin < n_cand ? (n_cand - j_begin < chunk_rows ? n_cand - j_begin : chunk_rows) : 0);
+  const int n_tiles = (n_rows + kT - 1) / kT;
   const uint16_t* win = static_cast<const uint16_t*>(a.win) + int64_t(b) * a.Wcap * kD;
   const uint16_t* cmp = static_cast<const uint16_t*>(a.cmp) + int64_t(b) * a.Ncap * kD;
+  // a readable 1 KiB row (the query's first head) stands in for a missing
+  // candidate: its score is masked, and its finite values keep 0 * row = 0
+  const uint16_t* filler = static_cast<const uint16_t*>(a.q) + qi * kH * kD;
 
-  // Q^T operand: Q[head][ks*32 + g*8 .. +7], 16 K-steps.
-  bf16x8 qb[16];
-  {
-    const uint16_t* q = static_cast<const uint16_t*>(a.q) + (qi * kH + head) * kD + g * 8;
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) qb[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(q + ks * 32));
-  }
-  // CSA: resolve the chunk's selections once, so that tile gathers never wait
-  // on a dependent index load.
+  // CSA: resolve the chunk's selections once, so that row copies never wait
+  // on a dependent index load
   if constexpr (!HCA) {
-    for (int j = tid; j < n_rows; j += 256) codes[j] = cand_code(a, false, c, qi, j_begin + j);
-    __syncthreads();
+    for (int j = tid; j < n_rows; j += kThreads) codes[j] = cand_code(a, false, c, qi, j_begin + j);
   }
-
-  const float qk_scale = a.scale * kLog2e;
-  const float sink2 = a.sink[head] * kLog2e;
-  // m_run is a reference maximum: it moves only when some head's running max
-  // exceeds it by more than 2^8 (lazy rescale), so exponentials stay <= 256
-  // and the 128-accumulator rescale runs on very few tiles.
-  float m_run, l_run;
-  if constexpr (!SPLIT) { m_run = sink2; l_run = g == 0 ? 1.f : 0.f; }
-  else { m_run = -1e30f; l_run = 0.f; }
-  floatx4 acc[32];
+  if (tid == 0) over_flag = 0;
+  if (tid < kH) mref[tid] = sink_ref(a.sink, tid);
+  __syncthreads();
+  const uint32_t lds_tiles = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)&tiles[0][0]));
+  // wave w copies rows kCopyRows*w .. +kCopyRows-1 of tile t (always exactly
+  // kCopyRows copies, so that the copy count in flight is known) and records
+  // which of them exist
+  auto issue = [&](int t) {
+    const int buf = t % kBufs;
+    const int jl = t * kT + wave * kCopyRows + (lane % kCopyRows);
+    int code = -1;
+    if (jl < n_rows) code = HCA ? cand_code(a, true, c, qi, j_begin + jl) : codes[jl];
+    const uint64_t ok = __ballot(code != -1);
+    if (lane == 0) vmask[buf][wave] = uint8_t(ok & ((1u << kCopyRows) - 1u));
+    const uint32_t dst = lds_tiles + uint32_t(buf * kT * kPitch + wave * kCopyRows * kPitch);
+    const uint32_t voff = uint32_t(lane ^ row_swap(wave * kCopyRows)) * 16u;
 #pragma unroll
-  for (int mt = 0; mt < 32; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  // gather geometry: thread owns 8 dims (dc*8..) of 8 rows (rg*8..) of a tile
-  const int dc = tid % 64, rg = tid / 64;
-  auto gather = [&](int jl0, uint4 (&v)[8]) -> unsigned {
-    unsigned mask = 0;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int jl = jl0 + rg * 8 + r;
-      int code = -1;
-      if (jl < n_rows) code = HCA ? cand_code(a, true, c, qi, j_begin + jl) : codes[jl];
-      const uint16_t* src = code >= 0 ? cmp + int64_t(code) * kD : (code <= -2 ? win + int64_t(-2 - code) * kD : nullptr);
-      if (src != nullptr) {
-        v[r] = *reinterpret_cast<const uint4*>(src + dc * 8);
-        mask |= 1u << r;
-      } else {
-        v[r] = uint4{0, 0, 0, 0};
-      }
+    for (int u = 0; u < kCopyRows; ++u) {
+      const int cu = __builtin_amdgcn_readlane(code, u);
+      const uint16_t* src = cu >= 0 ? cmp + int64_t(cu) * kD : (cu <= -2 ? win + int64_t(-2 - cu) * kD : filler);
+      copy_row_to_lds(src, voff, dst + uint32_t(u * kPitch));
     }
-    return mask;
   };
+  // top of tile step s: tile s has landed (only tile s+1's copies may still
+  // be in flight), then the barrier publishes it and frees tile s-2's buffer
+  auto step_sync = [&](int s) {
+    if (s + 1 < n_tiles) wait_vmem<kCopyRows>();
+    else wait_vmem<0>();
+    __syncthreads();
+    if (s + 2 < n_tiles) issue(s + 2);
+  };
+  const float qk_scale = a.scale * kLog2e;
 
-  uint4 v[8];
-  unsigned vmask = n_rows > 0 ? gather(0, v) : 0u;
-  for (int jl0 = 0; jl0 < n_rows; jl0 += kTile) {
+  if (wave < 4) {
+    // ===================== QK waves =====================
+    const int hh = wave & 1, rr = wave >> 1;  // heads hh*32.., rows rr*16.. of a tile
+    bf16x8 qb[2][16];  // Q^T: Q[hh*32 + ht*16 + c16][ks*32 + g*8 .. +7]
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
-      *reinterpret_cast<uint4*>(&Kt[kt_off(rg * 8 + r, dc)]) = v[r];
-    // transpose the 8x8 block: Vt[dim][rows rg*8 .. +7]
+    for (int ht = 0; ht < 2; ++ht) {
+      const uint16_t* q = static_cast<const uint16_t*>(a.q) + (qi * kH + hh * 32 + ht * 16 + c16) * kD + g * 8;
 #pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      uint32_t w4[4];
+      for (int ks = 0; ks < 16; ++ks) qb[ht][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(q + ks * 32));
+    }
+    const int k_off = (rr * 16 + c16) * kPitch + ((g ^ row_swap(c16)) << 4);
+    float m_ref[2];
 #pragma unroll
-      for (int rp = 0; rp < 4; ++rp) {
-        const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&v[2 * rp]);
-        const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&v[2 * rp + 1]);
-        const uint32_t x0 = a0[dd / 2], x1 = a1[dd / 2];
-        w4[rp] = (dd & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
+    for (int ht = 0; ht < 2; ++ht) m_ref[ht] = sink_ref(a.sink, hh * 32 + ht * 16 + c16);
+    for (int pass = 0; pass < 2; ++pass) {
+      float l_run[2], m_run[2];
+      bool over = false;
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) {
+        const float s2 = a.sink[hh * 32 + ht * 16 + c16] * kLog2e;
+        l_run[ht] = (!SPLIT && rr == 0 && g == 0) ? fast_exp2(s2 - m_ref[ht]) : 0.f;
+        m_run[ht] = -INFINITY;
       }
-      *reinterpret_cast<uint4*>(&Vt[vt_off(dc * 8 + dd) + rg * 8]) = uint4{w4[0], w4[1], w4[2], w4[3]};
-    }
-    if (dc == 0) {
+      if (n_tiles > 0) issue(0);
+      if (n_tiles > 1) issue(1);
+      for (int s = 0; s <= n_tiles; ++s) {
+        step_sync(s);
+        if (s == n_tiles) break;
+        const unsigned char* tile = tiles[s % kBufs];
+        const uint32_t okm = *reinterpret_cast<const uint32_t*>(&vmask[s % kBufs][rr * 4]);  // rows rr*16 + 4*w' + u
+        // ---- S^T = K . Q^T, K operands kAheadK K-steps ahead
+        floatx4 st[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+        bf16x8 kr[kAheadK + 1];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) valid[rg * 8 + r] = (vmask >> r) & 1u;
-    }
-    __syncthreads();
-    // the next tile's rows stream in while this one is multiplied
-    if (jl0 + kTile < n_rows) vmask = gather(jl0 + kTile, v);
-
-    // S^T tiles: tile t covers candidate rows (m/4)*8 + t*4 + m%4
-    float s8[8];
+        for (int ks = 0; ks < kAheadK; ++ks) kr[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(tile + k_off + ks * 64));
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int arow = (r16 / 4) * 8 + t * 4 + (r16 % 4);
-      floatx4 st = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < 16; ++ks) {
+          if (ks + kAheadK < 16)
+            kr[(ks + kAheadK) % (kAheadK + 1)] =
+                as_bf16x8(*reinterpret_cast<const uint4*>(tile + k_off + (ks + kAheadK) * 64));
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks)
-        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            as_bf16x8(*reinterpret_cast<const uint4*>(&Kt[kt_off(arow, ks * 4 + g)])), qb[ks], st, 0, 0, 0);
+          for (int ht = 0; ht < 2; ++ht)
+            st[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[ks % (kAheadK + 1)], qb[ht][ks], st[ht], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // ---- P = exp2(S - m): rows rr*16 + g*4 + i, head hh*32 + ht*16 + c16
+        uint16_t* pw = &pt[s & 1][0];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s8[t * 4 + i] = st[i];
-    }
-    // lane holds rows g*8 + 0..7 of head `head`
-    float tmax = -INFINITY;
+        for (int ht = 0; ht < 2; ++ht) {
+          float p[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      s8[i] = valid[g * 8 + i] ? s8[i] * qk_scale : -INFINITY;
-      tmax = fmaxf(tmax, s8[i]);
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-    if (__any(tmax > m_run + 8.f)) {  // wave-uniform: rescale every head of the wave
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha = fast_exp2(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int mt = 0; mt < 32; ++mt) acc[mt] *= alpha;
-      m_run = m_new;
-    }
-    float psum = 0.f;
-    uint32_t pw[4];
-#pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      const float p0 = fast_exp2(s8[i] - m_run), p1 = fast_exp2(s8[i + 1] - m_run);
-      psum += p0 + p1;
-      pw[i / 2] = pack_bf16x2(p0, p1);
-    }
-    l_run += psum;
-    const bf16x8 pb = as_bf16x8(uint4{pw[0], pw[1], pw[2], pw[3]});
-#pragma unroll
-    for (int mt = 0; mt < 32; ++mt) {
-      const bf16x8 va = as_bf16x8(*reinterpret_cast<const uint4*>(&Vt[vt_off(mt * 16 + r16) + g * 8]));
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, acc[mt], 0, 0, 0);
-    }
-    __syncthreads();
-  }
-
-  l_run += __shfl_xor(l_run, 16, kWave);
-  l_run += __shfl_xor(l_run, 32, kWave);
-  // lane holds O^T[dims mt*16 + g*4 + i][head]
-  if constexpr (!SPLIT) {
-    const int rope0 = kD - a.rope_dim;
-    for (int i = tid; i < a.rope_dim / 2; i += 256) {
-      float cs, sn;
-      rope_cos_sin(c.p, i, a.rope_dim, a.rope_base, &cs, &sn);
-      rope_cs[2 * i] = cs;
-      rope_cs[2 * i + 1] = sn;
-    }
-    __syncthreads();
-    const float inv_l = 1.f / l_run;
-    const int64_t obase = (qi * kH + head) * kD;
-#pragma unroll
-    for (int mt = 0; mt < 32; ++mt) {
-      float o[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = acc[mt][i] * inv_l;
-      const int d0 = mt * 16 + g * 4;
-      if (d0 >= rope0 && c.p >= 0) {
-#pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-          const int pi = (d0 + i - rope0) / 2;
-          const float cs = rope_cs[2 * pi], sn = rope_cs[2 * pi + 1];
-          const float x0 = o[i], x1 = o[i + 1];
-          o[i] = x0 * cs + x1 * sn;
-          o[i + 1] = x1 * cs - x0 * sn;
+          for (int i = 0; i < 4; ++i) {
+            const bool ok = (okm >> (8 * g + i)) & 1u;  // byte g of okm = wave rr*4 + g, bit i
+            const float sv = ok ? st[ht][i] * qk_scale : -INFINITY;
+            m_run[ht] = fmaxf(m_run[ht], sv);
+            p[i] = fast_exp2(sv - m_ref[ht]);
+          }
+          over = over || (m_run[ht] > m_ref[ht] + kHeadroom);
+          l_run[ht] += (p[0] + p[1]) + (p[2] + p[3]);
+          *reinterpret_cast<uint2*>(&pw[(hh * 32 + ht * 16 + c16) * kPPitch + rr * 16 + g * 4]) =
+              uint2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
         }
       }
-      if (a.out_dtype == CSA_BF16) {
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + obase + d0) =
-            uint2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-      } else {
-        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + obase + d0) = float4{o[0], o[1], o[2], o[3]};
+      // ---- per-head sums and maxima of this wave's rows
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) {
+        float l = l_run[ht] + __shfl_xor(l_run[ht], 16, kWave);
+        l += __shfl_xor(l, 32, kWave);
+        float m = fmaxf(m_run[ht], __shfl_xor(m_run[ht], 16, kWave));
+        m = fmaxf(m, __shfl_xor(m, 32, kWave));
+        if (g == 0) {
+          lsum[rr][hh * 32 + ht * 16 + c16] = l;
+          mseen[rr][hh * 32 + ht * 16 + c16] = m;
+        }
       }
+      if (__any(over) && lane == 0) over_flag = 1;
+      __syncthreads();
+      if (over_flag == 0) break;
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) {
+        const int h = hh * 32 + ht * 16 + c16;
+        m_ref[ht] = fmaxf(sink_ref(a.sink, h), fmaxf(mseen[0][h], mseen[1][h]));
+        if (rr == 0 && g == 0) mref[h] = m_ref[ht];
+      }
+      __syncthreads();  // every wave has read the flag and the maxima
+      if (tid == 0) over_flag = 0;
     }
   } else {
-    float* ws_o = static_cast<float*>(a.ws);
-    float* ws_ml = ws_o + int64_t(a.B) * a.S * nsplit * kH * kD;
-    const int64_t slot = (qi * nsplit + split) * kH + head;
+    // ===================== PV waves =====================
+    const int pv = wave - 4;  // dims pv*128 .. +128
+    // V^T operand: rows g*8 + h*4 + c16/4 (h = half of the 8-row K-slice),
+    // dims pv*128 + dt*16 + 4*(c16 % 4) .. +3
+    const int v_lo = (g * 8 + (c16 >> 2)) * kPitch + pv * 256 + (((c16 >> 1) & 1) << 4) + ((c16 & 1) << 3);
+    const int v_hi = (g * 8 + 4 + (c16 >> 2)) * kPitch + pv * 256 + ((((c16 >> 1) & 1) ^ 1) << 4) + ((c16 & 1) << 3);
+    floatx4 acc[8][4];  // O^T[dims pv*128 + dt*16 + g*4 + i][head ht*16 + c16]
+    for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int mt = 0; mt < 32; ++mt)
-      *reinterpret_cast<floatx4*>(ws_o + slot * kD + mt * 16 + g * 4) = acc[mt];
-    if (g == 0) {
-      ws_ml[2 * slot] = m_run;
-      ws_ml[2 * slot + 1] = l_run;
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) acc[dt][ht] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (n_tiles > 0) issue(0);
+      if (n_tiles > 1) issue(1);
+      for (int s = 0; s <= n_tiles; ++s) {
+        step_sync(s);
+        if (s == 0) continue;
+        const unsigned char* tile = tiles[(s - 1) % kBufs];
+        const uint16_t* pr = &pt[(s - 1) & 1][0];
+        bf16x8 pb[4];  // P^T[rows g*8 .. +7][head ht*16 + c16]
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht)
+          pb[ht] = as_bf16x8(*reinterpret_cast<const uint4*>(&pr[(ht * 16 + c16) * kPPitch + g * 8]));
+        bf16x8 vr[kAheadV + 1];
+        auto vload = [&](int dt, bf16x8& dst) {
+          const uint2 lo = lds_read_tr16(tile + v_lo + dt * 32);
+          const uint2 hi = lds_read_tr16(tile + v_hi + dt * 32);
+          dst = as_bf16x8(uint4{lo.x, lo.y, hi.x, hi.y});
+        };
+#pragma unroll
+        for (int dt = 0; dt < kAheadV; ++dt) vload(dt, vr[dt]);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          if (dt + kAheadV < 8) vload(dt + kAheadV, vr[(dt + kAheadV) % (kAheadV + 1)]);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int ht = 0; ht < 4; ++ht)
+            acc[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr[dt % (kAheadV + 1)], pb[ht], acc[dt][ht], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __syncthreads();  // the QK waves' sums, maxima and overflow flag
+      if (over_flag == 0) break;
+      __syncthreads();
+    }
+    float L[4];
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) L[ht] = lsum[0][ht * 16 + c16] + lsum[1][ht * 16 + c16];
+    if constexpr (!SPLIT) {
+      const int rope0 = kD - a.rope_dim;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const int d0 = pv * 128 + dt * 16 + g * 4;
+        float cs[2] = {1.f, 1.f}, sn[2] = {0.f, 0.f};
+        const bool rot = d0 >= rope0 && c.p >= 0;
+        if (rot) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u) rope_cos_sin(c.p, (d0 + 2 * u - rope0) / 2, a.rope_dim, a.rope_base, &cs[u], &sn[u]);
+        }
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) {
+          const float inv_l = 1.f / L[ht];
+          float o[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = acc[dt][ht][i] * inv_l;
+          if (rot) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const float x0 = o[2 * u], x1 = o[2 * u + 1];
+              o[2 * u] = x0 * cs[u] + x1 * sn[u];
+              o[2 * u + 1] = x1 * cs[u] - x0 * sn[u];
+            }
+          }
+          const int64_t off = (qi * kH + ht * 16 + c16) * kD + d0;
+          if (a.out_dtype == CSA_BF16) {
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + off) =
+                uint2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+          } else {
+            *reinterpret_cast<float4*>(static_cast<float*>(a.out) + off) = float4{o[0], o[1], o[2], o[3]};
+          }
+        }
+      }
+    } else {
+      float* ws_o = static_cast<float*>(a.ws);
+      const int64_t slot0 = (qi * nsplit + split) * kH;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht)
+          *reinterpret_cast<floatx4*>(ws_o + (slot0 + ht * 16 + c16) * kD + pv * 128 + dt * 16 + g * 4) = acc[dt][ht];
+    }
+  }
+  if constexpr (SPLIT) {
+    // reference (of the final pass) and sum per head
+    if (tid < kH) {
+      float* ws_ml = static_cast<float*>(a.ws) + int64_t(a.B) * a.S * nsplit * kH * kD;
+      const int64_t slot = (qi * nsplit + split) * kH + tid;
+      ws_ml[2 * slot] = mref[tid];
+      ws_ml[2 * slot + 1] = lsum[0][tid] + lsum[1][tid];
     }
   }
 }
@@ -457,12 +575,16 @@ AttnPlan plan_attn(int B, int S, int H, int D, int max_cand, int dtype, bool hca
   if (want > kMaxSplits) want = kMaxSplits;
   if (want < 1) want = 1;
   int64_t rows = (max_cand + want - 1) / want;
-  rows = (rows + kTile - 1) / kTile * kTile;
-  if (rows < kTile) rows = kTile;
+  rows = (rows + kSplitGrain - 1) / kSplitGrain * kSplitGrain;
+  if (rows < kSplitGrain) rows = kSplitGrain;
   if (!hca && rows > kMaxChunk) rows = kMaxChunk;
   p.chunk_rows = int(rows);
   p.nsplit = int((max_cand + rows - 1) / rows);
   if (p.nsplit < 1) p.nsplit = 1;
+  if (p.nsplit > kMaxSplits) {  // more CSA candidates than the split table holds
+    p = AttnPlan{false, 1, 0, 0};
+    return p;
+  }
   if (p.nsplit > 1)
     p.ws_bytes = size_t(nq) * p.nsplit * kH * (size_t(kD) + 2) * sizeof(float);
   return p;
@@ -474,10 +596,10 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, bool hca, hipStr
   if (plan.mfma) {
     const dim3 grid(unsigned(nq), plan.nsplit);
     const bool split = plan.nsplit > 1;
-    if (hca && split) hipLaunchKernelGGL((attn_mfma<true, true>), grid, dim3(256), 0, stream, a, plan.nsplit, plan.chunk_rows);
-    else if (hca) hipLaunchKernelGGL((attn_mfma<true, false>), grid, dim3(256), 0, stream, a, plan.nsplit, plan.chunk_rows);
-    else if (split) hipLaunchKernelGGL((attn_mfma<false, true>), grid, dim3(256), 0, stream, a, plan.nsplit, plan.chunk_rows);
-    else hipLaunchKernelGGL((attn_mfma<false, false>), grid, dim3(256), 0, stream, a, plan.nsplit, plan.chunk_rows);
+    if (hca && split) hipLaunchKernelGGL((attn_mfma<true, true>), grid, dim3(kThreads), 0, stream, a, plan.nsplit, plan.chunk_rows);
+    else if (hca) hipLaunchKernelGGL((attn_mfma<true, false>), grid, dim3(kThreads), 0, stream, a, plan.nsplit, plan.chunk_rows);
+    else if (split) hipLaunchKernelGGL((attn_mfma<false, true>), grid, dim3(kThreads), 0, stream, a, plan.nsplit, plan.chunk_rows);
+    else hipLaunchKernelGGL((attn_mfma<false, false>), grid, dim3(kThreads), 0, stream, a, plan.nsplit, plan.chunk_rows);
     if (plan.nsplit > 1)
       hipLaunchKernelGGL(attn_combine, dim3(unsigned(nq), kH / 4), dim3(256), 0, stream, a, plan.nsplit);
   } else {

@@ -91,4 +91,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 // <= 0; results below 2^-126 flush to zero, which is harmless for weights.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max(x, 0) as one integer max on the bit pattern: a set sign bit makes the
+// pattern a negative integer, so every negative value (and -0) becomes +0 and
+// every other value passes unchanged.  fmaxf would add a NaN-quieting max.
+__device__ __forceinline__ float relu(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
 }  // namespace csa

@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kWave* kStreamWaves) void index_stream(IndexArgs a)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) part += fmaxf(acc[mt][i], 0.f) * wv[mt][i];
+        for (int i = 0; i < 4; ++i) part += relu(acc[mt][i]) * wv[mt][i];
       part += __shfl_xor(part, 16, kWave);
       part += __shfl_xor(part, 32, kWave);
       const int64_t e = base + blk * 16 + r16;
@@ -239,8 +239,10 @@ __global__ __launch_bounds__(kWave* kStreamWaves) void index_tile(IndexArgs a, i
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           const float4 w4 = *reinterpret_cast<const float4*>(wq + mt * 16);
-          part += fmaxf(acc[nt][mt][0], 0.f) * w4.x + fmaxf(acc[nt][mt][1], 0.f) * w4.y +
-                  fmaxf(acc[nt][mt][2], 0.f) * w4.z + fmaxf(acc[nt][mt][3], 0.f) * w4.w;
+          part += relu(acc[nt][mt][0]) * w4.x;
+          part += relu(acc[nt][mt][1]) * w4.y;
+          part += relu(acc[nt][mt][2]) * w4.z;
+          part += relu(acc[nt][mt][3]) * w4.w;
         }
         part += __shfl_xor(part, 16, kWave);
         part += __shfl_xor(part, 32, kWave);
