@@ -51,13 +51,13 @@ constexpr int kWaves = 8;   // 4 QK + 4 PV waves
 constexpr int kThreads = kWaves * kWave;
 constexpr int kCopyRows = kT / kWaves;  // rows each wave copies per tile
 constexpr int kRowBytes = kD * 2;
-// LDS row pitch 1 KiB + 32 B (consecutive rows start 8 banks apart) and, in
-// rows with bit 2 set, the two 16-byte chunks of each 32-byte pair swapped.
-// Then the 8 rows one 128-bit K read serves per cycle, and the 4 rows x 2
-// chunks one transposing V read serves per cycle, all fall on distinct banks,
-// while every per-step offset stays an immediate.
+// LDS tile layout (measured bank-conflict free on gfx950 for both the
+// 128-bit K reads and the transposing V reads): row pitch 1 KiB + 32 B, and
+// in rows whose bits 2 and 3 differ, 16-byte chunk c of the row is stored at
+// chunk c ^ 8.  Every per-step offset is then an immediate added to one of
+// two per-lane bases.
 constexpr int kPitch = kRowBytes + 32;
-__device__ __forceinline__ int row_swap(int r) { return (r >> 2) & 1; }
+__device__ __forceinline__ int row_flip(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
 constexpr int kPPitch = kT + 8;   // bf16 per head row of P in LDS (80 B: 8 heads on distinct banks)
 constexpr int kAheadK = 4;        // K operand prefetch distance, in K-steps
 constexpr int kAheadV = 3;        // V^T operand prefetch distance, in dim tiles
@@ -74,7 +74,11 @@ constexpr int kMaxSplits = 256;
 // buffers behind it; the kernel waits for these copies itself before the
 // barrier that publishes a tile.
 __device__ __forceinline__ void copy_row_to_lds(const void* row, uint32_t voff, uint32_t lds_row) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(row), "{m0}"(lds_row) : "memory");
+  // the row address is wave-uniform; readfirstlane states it so it can sit in SGPRs
+  const uint64_t r = reinterpret_cast<uint64_t>(row);
+  const uint64_t su = uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(r)))) |
+                      (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(r >> 32)))) << 32);
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(su), "{m0}"(lds_row) : "memory");
 }
 // s_waitcnt with only the vector-memory count set (expcnt, lgkmcnt: no wait)
 template <int N>
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
     const uint64_t ok = __ballot(code != -1);
     if (lane == 0) vmask[buf][wave] = uint8_t(ok & ((1u << kCopyRows) - 1u));
     const uint32_t dst = lds_tiles + uint32_t(buf * kT * kPitch + wave * kCopyRows * kPitch);
-    const uint32_t voff = uint32_t(lane ^ row_swap(wave * kCopyRows)) * 16u;
+    const uint32_t voff = uint32_t(lane ^ (row_flip(wave * kCopyRows) << 3)) * 16u;  // same for the wave's rows
 #pragma unroll
     for (int u = 0; u < kCopyRows; ++u) {
       const int cu = __builtin_amdgcn_readlane(code, u);
@@ -236,7 +240,10 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) qb[ht][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(q + ks * 32));
     }
-    const int k_off = (rr * 16 + c16) * kPitch + ((g ^ row_swap(c16)) << 4);
+    // K chunk ks*4 + g of row rr*16 + c16 sits 128 B further (K-steps with
+    // bit 1 clear) or nearer (bit 1 set) when the row is flipped
+    const int k_base = (rr * 16 + c16) * kPitch + g * 16;
+    const int k_off0 = k_base + row_flip(c16) * 128, k_off1 = k_base - row_flip(c16) * 128;
     float m_ref[2];
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht) m_ref[ht] = sink_ref(a.sink, hh * 32 + ht * 16 + c16);
@@ -260,12 +267,13 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
         floatx4 st[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
         bf16x8 kr[kAheadK + 1];
 #pragma unroll
-        for (int ks = 0; ks < kAheadK; ++ks) kr[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(tile + k_off + ks * 64));
+        for (int ks = 0; ks < kAheadK; ++ks)
+          kr[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(tile + ((ks & 2) ? k_off1 : k_off0) + ks * 64));
 #pragma unroll
         for (int ks = 0; ks < 16; ++ks) {
           if (ks + kAheadK < 16)
-            kr[(ks + kAheadK) % (kAheadK + 1)] =
-                as_bf16x8(*reinterpret_cast<const uint4*>(tile + k_off + (ks + kAheadK) * 64));
+            kr[(ks + kAheadK) % (kAheadK + 1)] = as_bf16x8(*reinterpret_cast<const uint4*>(
+                tile + (((ks + kAheadK) & 2) ? k_off1 : k_off0) + (ks + kAheadK) * 64));
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int ht = 0; ht < 2; ++ht)
@@ -318,9 +326,12 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
     // ===================== PV waves =====================
     const int pv = wave - 4;  // dims pv*128 .. +128
     // V^T operand: rows g*8 + h*4 + c16/4 (h = half of the 8-row K-slice),
-    // dims pv*128 + dt*16 + 4*(c16 % 4) .. +3
-    const int v_lo = (g * 8 + (c16 >> 2)) * kPitch + pv * 256 + (((c16 >> 1) & 1) << 4) + ((c16 & 1) << 3);
-    const int v_hi = (g * 8 + 4 + (c16 >> 2)) * kPitch + pv * 256 + ((((c16 >> 1) & 1) ^ 1) << 4) + ((c16 & 1) << 3);
+    // dims pv*128 + dt*16 + 4*(c16 % 4) .. +3; a flipped row (bit 2 = h,
+    // bit 3 = g & 1) holds the chunk 128 B further (dt < 4) or nearer (dt >= 4)
+    const int v_base = (g * 8 + (c16 >> 2)) * kPitch + pv * 256 + (((c16 >> 1) & 1) << 4) + ((c16 & 1) << 3);
+    const int f_lo = (g & 1) * 128, f_hi = ((g & 1) ^ 1) * 128;
+    const int v_lo0 = v_base + f_lo, v_lo1 = v_base - f_lo;
+    const int v_hi0 = v_base + 4 * kPitch + f_hi, v_hi1 = v_base + 4 * kPitch - f_hi;
     floatx4 acc[8][4];  // O^T[dims pv*128 + dt*16 + g*4 + i][head ht*16 + c16]
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -340,8 +351,8 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
           pb[ht] = as_bf16x8(*reinterpret_cast<const uint4*>(&pr[(ht * 16 + c16) * kPPitch + g * 8]));
         bf16x8 vr[kAheadV + 1];
         auto vload = [&](int dt, bf16x8& dst) {
-          const uint2 lo = lds_read_tr16(tile + v_lo + dt * 32);
-          const uint2 hi = lds_read_tr16(tile + v_hi + dt * 32);
+          const uint2 lo = lds_read_tr16(tile + ((dt & 4) ? v_lo1 : v_lo0) + dt * 32);
+          const uint2 hi = lds_read_tr16(tile + ((dt & 4) ? v_hi1 : v_hi0) + dt * 32);
           dst = as_bf16x8(uint4{lo.x, lo.y, hi.x, hi.y});
         };
 #pragma unroll

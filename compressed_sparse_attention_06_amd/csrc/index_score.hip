@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kWave* kStreamWaves) void index_stream(IndexArgs a)
 // ---------------------------------------------------------------------------
 // Tile kernel (many queries per sequence, e.g. prefill): grid 1-D, 8 waves.
 // A block owns 32 queries x 512 index rows.  The rows are staged once into
-// LDS (row pitch padded by 16 bytes so that the 16 rows of a fragment sit on
+// LDS (row pitch padded by 32 bytes so that the 16 rows of a fragment sit on
 // different banks); after that single barrier every wave runs on its own:
 // it holds one query's 64x128 operand in VGPRs (the next query's operand in
 // flight), streams 16-row tiles of the block's rows from LDS as MFMA B
@@ -159,7 +159,7 @@ constexpr int kTileQ = 32;
 constexpr int kTileE = 512;
 constexpr int kXcd = 8;
 constexpr int kRowVec = kDI / 8;      // uint4 per index row
-constexpr int kRowPitch = kRowVec + 1;
+constexpr int kRowPitch = kRowVec + 2;  // 288 B: 16 rows of one 16-byte column fall on distinct banks
 
 constexpr int kNT = 2;  // 16-row tiles per MFMA step of the tile kernel
 
