@@ -14,10 +14,9 @@
 //    from HBM into registers (every load instruction covers 64 contiguous
 //    bytes of 16 rows), 4 x 16x16x32 MFMA per 16 rows and K-step, then ReLU,
 //    head weights and a two-step cross-lane sum.
-//  * index_tile (many queries per sequence, e.g. prefill): a workgroup stages
-//    512 index rows in LDS once; each wave then scores its own queries
-//    against them without further barriers, stopping at each query's causal
-//    bound.
+//  * index_tile (many queries per sequence, e.g. prefill): the query
+//    operands stay in registers and the index rows stream past them through
+//    LDS up to the workgroup's causal bound.
 //
 // A and B share the K order of a K-step: lane group g, element i <-> dim
 // ks*32 + g*8 + i.
@@ -144,126 +143,137 @@ __global__ __launch_bounds__(kWave* kStreamWaves) void index_stream(IndexArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Tile kernel (many queries per sequence, e.g. prefill): grid 1-D, 8 waves.
-// A block owns 32 queries x 512 index rows.  The rows are staged once into
-// LDS (row pitch padded by 32 bytes so that the 16 rows of a fragment sit on
-// different banks); after that single barrier every wave runs on its own:
-// it holds one query's 64x128 operand in VGPRs (the next query's operand in
-// flight), streams 16-row tiles of the block's rows from LDS as MFMA B
-// operands, and stops at the query's causal bound.  The entry tiles of one
-// query chunk go to one XCD back to back (workgroups are dealt round-robin
-// over the 8 XCDs), so a chunk's query operands come from HBM once and then
-// from that XCD's L2.
+// Tile kernel (many queries per sequence, e.g. prefill): grid 1-D, 4 waves,
+// three workgroups per CU.  A workgroup owns 4 consecutive queries of one
+// sequence; wave w keeps query w's 64x128 operand in VGPRs for the whole run
+// and the index rows stream past it through LDS in chunks of 64 rows
+// (copied HBM -> LDS by the load unit, double-buffered), up to the largest
+// causal bound of the 4 queries.  Each K fragment read from LDS feeds the 4
+// head tiles of the wave's query.  LDS rows are 256 B with 16-byte chunk c of
+// row r stored at chunk c ^ (r % 16), so the 16 rows of one fragment fall on
+// distinct banks.  Scores are staged in LDS and written one chunk later as
+// coalesced 16-byte stores.  Workgroups are taken heaviest first (the last
+// queries see the most rows).
 // ---------------------------------------------------------------------------
-constexpr int kTileQ = 32;
-constexpr int kTileE = 512;
-constexpr int kXcd = 8;
-constexpr int kRowVec = kDI / 8;      // uint4 per index row
-constexpr int kRowPitch = kRowVec + 2;  // 288 B: 16 rows of one 16-byte column fall on distinct banks
+constexpr int kTQ = 4;          // queries per workgroup (one per wave)
+constexpr int kTWaves = 4;
+constexpr int kTThreads = kTWaves * kWave;
+constexpr int kCR = 64;         // index rows per chunk
+constexpr int kRowB = kDI * 2;  // bytes per index row
+constexpr int kCopyPerWave = kCR / kTWaves / 4;  // 4 rows per LDS copy instruction
 
-constexpr int kNT = 2;  // 16-row tiles per MFMA step of the tile kernel
+typedef __attribute__((address_space(3))) void lds_void;
+// One LDS copy instruction: lane l moves the 16 bytes at base + voff[l] to
+// LDS address lds + 16 l (M0 carries lds).  The kernel waits for it itself.
+__device__ __forceinline__ void copy_to_lds(const void* base, uint32_t voff, uint32_t lds) {
+  const uint64_t r = reinterpret_cast<uint64_t>(base);
+  const uint64_t su = uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(r)))) |
+                      (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(r >> 32)))) << 32);
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(su), "{m0}"(lds) : "memory");
+}
 
-__global__ __launch_bounds__(kWave* kStreamWaves) void index_tile(IndexArgs a, int qchunks_per_seq, int etiles,
-                                                                 int nchunks) {
-  __shared__ uint4 rows[kTileE * kRowPitch];
-  __shared__ float wsh[kTileQ][kHI];
-  __shared__ int svis[kTileQ];
-  constexpr int kThreads = kWave * kStreamWaves;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+__global__ __launch_bounds__(kTThreads, 3) void index_tile(IndexArgs a, int groups_per_seq, int ngroups) {
+  __shared__ __attribute__((aligned(16))) unsigned char rows[2][kCR * kRowB];
+  __shared__ __attribute__((aligned(16))) float sc[2][kTWaves][kCR];
+  __shared__ int svis[kTQ];
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int g = lane / 16, r16 = lane % 16;
-  const int xcd = blockIdx.x % kXcd, local = blockIdx.x / kXcd;
-  const int chunk = (local / etiles) * kXcd + xcd;
-  const int tile = local % etiles;
-  if (chunk >= nchunks) return;
-  const int b = chunk / qchunks_per_seq;
-  const int s0 = (chunk % qchunks_per_seq) * kTileQ;
-  const int nq = min(kTileQ, a.S - s0);
+  const int grp = ngroups - 1 - int(blockIdx.x);  // heaviest first
+  const int b = grp / groups_per_seq;
+  const int s0 = (grp % groups_per_seq) * kTQ;
+  const int nq = min(kTQ, a.S - s0);
   const int64_t q0 = int64_t(b) * a.S + s0;
   const int Ncap = a.Ncap;
-  const int e_blk = tile * kTileE;
-  const int e_end = min(e_blk + kTileE, Ncap);
-  if (tid < kTileQ) svis[tid] = tid < nq ? int(visible_entries(a.pos, q0 + tid, a.ratio, Ncap)) : 0;
+  if (tid < kTQ) svis[tid] = tid < nq ? int(visible_entries(a.pos, q0 + tid, a.ratio, Ncap)) : 0;
   __syncthreads();
   int vmax = 0;
   for (int j = 0; j < nq; ++j) vmax = max(vmax, svis[j]);
-  if (e_blk >= vmax) {  // no query of the chunk sees any row of the tile
-    for (int j = 0; j < nq; ++j)
-      for (int e = e_blk + tid; e < e_end; e += kThreads) a.scores[(q0 + j) * Ncap + e] = -INFINITY;
-    return;
-  }
-  // stage the visible part of the block's rows
-  {
-    const int n_rows = min(e_end, vmax) - e_blk;
-    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.cache) +
-                                                      (int64_t(b) * Ncap + e_blk) * kDI);
-    for (int i = tid; i < n_rows * kRowVec; i += kThreads) rows[(i / kRowVec) * kRowPitch + i % kRowVec] = src[i];
-    for (int i = tid; i < nq * kHI; i += kThreads) wsh[i / kHI][i % kHI] = a.w[q0 * kHI + i];
-  }
-  __syncthreads();
-
-  const uint4* qsrc = reinterpret_cast<const uint4*>(a.q_idx);
-  auto fetch = [&](int j, bf16x8 (&dst)[4][4]) {
-    const uint4* q = qsrc + (q0 + j) * (kHI * kRowVec);
+  const int n_chunks = (vmax + kCR - 1) / kCR;
+  const uint16_t* cache = static_cast<const uint16_t*>(a.cache) + int64_t(b) * Ncap * kDI;
+  const uint32_t lds_rows = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)&rows[0][0]));
+  // wave w copies rows 16w..16w+15 of a chunk, 4 rows per instruction; rows
+  // past the causal bound repeat the last visible row (finite, masked)
+  auto issue = [&](int c, int buf) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) dst[mt][ks] = as_bf16x8(q[(mt * 16 + r16) * kRowVec + ks * 4 + g]);
-  };
-  auto score_query = [&](int j, const bf16x8 (&qa)[4][4]) {
-    const float* wq = wsh[j] + g * 4;
-    const int nv = svis[j];
-    float* srow = a.scores + (q0 + j) * Ncap;
-    const int e_vis = min(e_end, nv);  // rows [e_blk, e_vis) are scored, the rest of the tile is -inf
-    for (int e = max(e_vis, e_blk) + lane; e < e_end; e += kWave) srow[e] = -INFINITY;
-    // kNT 16-row tiles (4*kNT independent accumulator chains) per step keep
-    // the matrix pipe fed; the ReLU / weight epilogue follows each step
-    for (int t0 = e_blk; t0 < e_vis; t0 += kNT * 16) {
-      floatx4 acc[kNT][4];  // [16-row tile][head tile]
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-          const bf16x8 kk = as_bf16x8(rows[(t0 - e_blk + nt * 16 + r16) * kRowPitch + g + ks * 4]);
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-            acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][ks], kk, acc[nt][mt], 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        float part = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const float4 w4 = *reinterpret_cast<const float4*>(wq + mt * 16);
-          part += relu(acc[nt][mt][0]) * w4.x;
-          part += relu(acc[nt][mt][1]) * w4.y;
-          part += relu(acc[nt][mt][2]) * w4.z;
-          part += relu(acc[nt][mt][3]) * w4.w;
-        }
-        part += __shfl_xor(part, 16, kWave);
-        part += __shfl_xor(part, 32, kWave);
-        const int e = t0 + nt * 16 + r16;
-        if (g == 0 && e < e_end) srow[e] = e < nv ? part : -INFINITY;
-      }
+    for (int u = 0; u < kCopyPerWave; ++u) {
+      const int rl = wave * (kCR / kTWaves) + u * 4 + g;  // row of this lane within the chunk
+      const int e = min(c * kCR + rl, vmax - 1);
+      const uint32_t voff = uint32_t(e) * kRowB + uint32_t(((r16 ^ (rl & 15)) << 4));
+      copy_to_lds(cache, voff, lds_rows + uint32_t(buf * kCR * kRowB + (wave * (kCR / kTWaves) + u * 4) * kRowB));
     }
   };
-  // wave w takes queries w, w+8, ...; two operand sets alternate so that the
-  // next query's operand is in flight while the current one is scored
-  bf16x8 qa0[4][4], qa1[4][4];
-  int j = wave;
-  if (j < nq) fetch(j, qa0);
-  while (j < nq) {
-    if (j + kStreamWaves < nq) fetch(j + kStreamWaves, qa1);
-    score_query(j, qa0);
-    j += kStreamWaves;
-    if (j >= nq) break;
-    if (j + kStreamWaves < nq) fetch(j + kStreamWaves, qa0);
-    score_query(j, qa1);
-    j += kStreamWaves;
+  if (n_chunks > 0) issue(0, 0);
+
+  // this wave's query (an absent one reuses query 0's operands; its scores are never stored)
+  const int nv = wave < nq ? svis[wave] : 0;
+  const int64_t qw = q0 + (wave < nq ? wave : 0);
+  bf16x8 qa[4][4];  // [head tile][K-step]: Q[mt*16 + r16][ks*32 + g*8 .. +7]
+  float wv[4][4];   // [head tile][i]: w[mt*16 + g*4 + i]
+  {
+    const uint4* q = reinterpret_cast<const uint4*>(a.q_idx) + qw * (kHI * kDI / 8);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qa[mt][ks] = as_bf16x8(q[(mt * 16 + r16) * (kDI / 8) + ks * 4 + g]);
+      const float4 w4 = *reinterpret_cast<const float4*>(a.w + qw * kHI + mt * 16 + g * 4);
+      wv[mt][0] = w4.x; wv[mt][1] = w4.y; wv[mt][2] = w4.z; wv[mt][3] = w4.w;
+    }
+  }
+  // K fragment offsets within a 16-row tile: row r16, chunk (ks*4 + g) ^ r16
+  int koff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) koff[ks] = r16 * kRowB + (((ks * 4 + g) ^ r16) << 4);
+
+  // scores of chunk c (staged in sc[c & 1]) go out at the start of chunk c+1:
+  // lanes 0..15 store rows 4*lane .. +3 of the wave's query
+  auto store_chunk = [&](int c) {
+    const int rw = lane * 4;
+    const int e = c * kCR + rw;
+    if (lane < kCR / 4 && wave < nq && e < Ncap)
+      *reinterpret_cast<float4*>(a.scores + qw * Ncap + e) = *reinterpret_cast<const float4*>(&sc[c & 1][wave][rw]);
+  };
+
+  for (int c = 0; c < n_chunks; ++c) {
+    const int buf = c & 1;
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): chunk c's copies (and older stores) are done
+    __syncthreads();  // every wave's copies landed; chunk c-1's buffer is free
+    if (c + 1 < n_chunks) issue(c + 1, buf ^ 1);
+    if (c > 0) store_chunk(c - 1);
+    const unsigned char* tb = rows[buf];
+    // 16-row tiles up to the workgroup's causal bound; the rest of the chunk is -inf
+    const int nt_end = min(kCR / 16, (vmax - c * kCR + 15) / 16);
+#pragma unroll 1
+    for (int nt = 0; nt < nt_end; ++nt) {
+      const int e0 = c * kCR + nt * 16;
+      bf16x8 kk[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kk[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(tb + nt * 16 * kRowB + koff[ks]));
+      floatx4 acc[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][0], kk[0], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+      for (int ks = 1; ks < 4; ++ks)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][ks], kk[ks], acc[mt], 0, 0, 0);
+      // lane holds heads mt*16 + g*4 + i of row e0 + r16
+      float part = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part += relu(acc[mt][i]) * wv[mt][i];
+      part += __shfl_xor(part, 16, kWave);
+      part += __shfl_xor(part, 32, kWave);
+      if (g == 0) sc[buf][wave][nt * 16 + r16] = e0 + r16 < nv ? part : -INFINITY;
+    }
+    for (int i = nt_end * 16 + lane; i < kCR; i += kWave) sc[buf][wave][i] = -INFINITY;
+  }
+  if (n_chunks > 0) store_chunk(n_chunks - 1);
+  // entries past the last chunk are invisible to every query of the group
+  for (int j = 0; j < nq; ++j) {
+    float* srow = a.scores + (q0 + j) * Ncap;
+    for (int e = n_chunks * kCR + tid; e < Ncap; e += kTThreads) srow[e] = -INFINITY;
   }
 }
 
@@ -299,13 +309,10 @@ __global__ __launch_bounds__(256) void index_any(IndexArgs a) {
 hipError_t launch_index_score(const IndexArgs& a, hipStream_t stream) {
   const int64_t nq = int64_t(a.B) * a.S;
   if (nq == 0 || a.Ncap == 0) return hipSuccess;
-  if (a.use_mfma && a.H == kHI && a.D == kDI && a.S >= 2 * kTileQ) {
-    const int qcs = (a.S + kTileQ - 1) / kTileQ;
-    const int nchunks = a.B * qcs;
-    const int etiles = (a.Ncap + kTileE - 1) / kTileE;
-    const int64_t nblocks = int64_t((nchunks + kXcd - 1) / kXcd) * kXcd * etiles;
-    hipLaunchKernelGGL(index_tile, dim3(unsigned(nblocks)), dim3(kWave * kStreamWaves), 0, stream, a, qcs, etiles,
-                       nchunks);
+  if (a.use_mfma && a.H == kHI && a.D == kDI && a.S >= 2 * kTQ && a.Ncap % 4 == 0) {
+    const int gps = (a.S + kTQ - 1) / kTQ;
+    const int ngroups = a.B * gps;
+    hipLaunchKernelGGL(index_tile, dim3(unsigned(ngroups)), dim3(kTThreads), 0, stream, a, gps, ngroups);
   } else if (a.use_mfma && a.H == kHI && a.D == kDI) {
     const int64_t blocks1 = nq * ((a.Ncap + kStepRows - 1) / kStepRows);
     if (blocks1 <= 4096) {
