@@ -91,6 +91,23 @@ constexpr float kLog2e = 1.4426950408889634f;
 // <= 0; results below 2^-126 flush to zero, which is harmless for weights.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Sum / max over the four 16-lane rows of a wave that share lane index
+// l % 16 (lanes l, l^16, l^32, l^48), register to register: each swap
+// exchanges one half of two copies of x, so adding (or max-ing) the pair
+// combines lanes l and l^32, then l and l^16.
+__device__ __forceinline__ float sum_rows4(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+__device__ __forceinline__ float max_rows4(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
 // max(x, 0) as one integer max on the bit pattern: a set sign bit makes the
 // pattern a negative integer, so every negative value (and -0) becomes +0 and
 // every other value passes unchanged.  fmaxf would add a NaN-quieting max.

@@ -120,8 +120,7 @@ __global__ __launch_bounds__(kWave* kStreamWaves) void index_stream(IndexArgs a)
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) part += relu(acc[mt][i]) * wv[mt][i];
-      part += __shfl_xor(part, 16, kWave);
-      part += __shfl_xor(part, 32, kWave);
+      part = sum_rows4(part);
       const int64_t e = base + blk * 16 + r16;
       if (g == 0 && e < Ncap) srow[e] = e < n_vis ? part : -INFINITY;
     }
@@ -241,15 +240,16 @@ __global__ __launch_bounds__(kTThreads, 3) void index_tile(IndexArgs a, int grou
     if (c + 1 < n_chunks) issue(c + 1, buf ^ 1);
     if (c > 0) store_chunk(c - 1);
     const unsigned char* tb = rows[buf];
-    // 16-row tiles up to the workgroup's causal bound; the rest of the chunk is -inf
-    const int nt_end = min(kCR / 16, (vmax - c * kCR + 15) / 16);
-#pragma unroll 1
-    for (int nt = 0; nt < nt_end; ++nt) {
-      const int e0 = c * kCR + nt * 16;
-      bf16x8 kk[4];
+    // The chunk's four 16-row tiles in one branch-free region: the MFMAs of
+    // tile nt+1 are interleaved with the ReLU / weight epilogue of tile nt
+    // (1 MFMA, then VALU work, ...), so the wave keeps issuing VALU while the
+    // matrix core works.  Rows past the causal bound are scored too (copies of
+    // a visible row) and masked to -inf.
+    auto kload = [&](int nt, bf16x8 (&kk)[4]) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) kk[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(tb + nt * 16 * kRowB + koff[ks]));
-      floatx4 acc[4];
+    };
+    auto mma = [&](const bf16x8 (&kk)[4], floatx4 (&acc)[4]) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
         acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][0], kk[0], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
@@ -257,17 +257,41 @@ __global__ __launch_bounds__(kTThreads, 3) void index_tile(IndexArgs a, int grou
       for (int ks = 1; ks < 4; ++ks)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][ks], kk[ks], acc[mt], 0, 0, 0);
-      // lane holds heads mt*16 + g*4 + i of row e0 + r16
-      float part = 0.f;
+    };
+    // lane holds heads mt*16 + g*4 + i of row c*kCR + nt*16 + r16
+    auto epi = [&](int nt, const floatx4 (&acc)[4]) {
+      float p4[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
+        p4[mt] = relu(acc[mt][0]) * wv[mt][0] + relu(acc[mt][1]) * wv[mt][1] + relu(acc[mt][2]) * wv[mt][2] +
+                 relu(acc[mt][3]) * wv[mt][3];
+      const float part = sum_rows4((p4[0] + p4[1]) + (p4[2] + p4[3]));
+      if (g == 0) sc[buf][wave][nt * 16 + r16] = c * kCR + nt * 16 + r16 < nv ? part : -INFINITY;
+    };
+    auto interleave = [&]() {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) part += relu(acc[mt][i]) * wv[mt][i];
-      part += __shfl_xor(part, 16, kWave);
-      part += __shfl_xor(part, 32, kWave);
-      if (g == 0) sc[buf][wave][nt * 16 + r16] = e0 + r16 < nv ? part : -INFINITY;
-    }
-    for (int i = nt_end * 16 + lane; i < kCR; i += kWave) sc[buf][wave][i] = -INFINITY;
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // then up to three VALU
+      }
+    };
+    bf16x8 kk[4];
+    floatx4 acc0[4], acc1[4];
+    kload(0, kk);
+    mma(kk, acc0);
+    kload(1, kk);
+    mma(kk, acc1);
+    epi(0, acc0);
+    interleave();
+    kload(2, kk);
+    mma(kk, acc0);
+    epi(1, acc1);
+    interleave();
+    kload(3, kk);
+    mma(kk, acc1);
+    epi(2, acc0);
+    interleave();
+    epi(3, acc1);
   }
   if (n_chunks > 0) store_chunk(n_chunks - 1);
   // entries past the last chunk are invisible to every query of the group
