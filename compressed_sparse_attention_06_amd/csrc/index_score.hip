@@ -275,20 +275,20 @@ __global__ __launch_bounds__(kTThreads, 3) void index_tile(IndexArgs a, int grou
         __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // then up to three VALU
       }
     };
-    bf16x8 kk[4];
+    bf16x8 ka[4], kb[4];  // K operands of the next two tiles
     floatx4 acc0[4], acc1[4];
-    kload(0, kk);
-    mma(kk, acc0);
-    kload(1, kk);
-    mma(kk, acc1);
+    kload(0, ka);
+    kload(1, kb);
+    mma(ka, acc0);
+    kload(2, ka);
+    mma(kb, acc1);
     epi(0, acc0);
     interleave();
-    kload(2, kk);
-    mma(kk, acc0);
+    kload(3, kb);
+    mma(ka, acc0);
     epi(1, acc1);
     interleave();
-    kload(3, kk);
-    mma(kk, acc1);
+    mma(kb, acc1);
     epi(2, acc0);
     interleave();
     epi(3, acc1);
