@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="csa_decode_64k", choices=sorted(synth.CONFIGS))
-    ap.add_argument("--extra", default="hca_decode_1m,csa_prefill_8k",
+    ap.add_argument("--extra", default="hca_decode_1m,csa_decode_1m,csa_prefill_8k",
                     help="comma-separated secondary workloads measured after the main one ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -81,6 +81,23 @@ def _f32(x, device):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
 
 
+def _fill_cache(dst, cid, tid, rows, device):
+    """dst[b, :rows[b]] = the seeded cache rows of sequence b, drawn chunk by
+    chunk on a thread pool (the generator releases the GIL while drawing)."""
+    from concurrent.futures import ThreadPoolExecutor
+    d = dst.shape[-1]
+    jobs = [(b, c) for b in range(dst.shape[0]) for c in range((int(rows[b]) + synth.CHUNK_ROWS - 1) // synth.CHUNK_ROWS)]
+
+    def one(job):
+        b, c = job
+        lo, hi = c * synth.CHUNK_ROWS, min((c + 1) * synth.CHUNK_ROWS, int(rows[b]))
+        blk = synth.cache_rows(cid, tid, b, hi, d, lo)
+        dst[b, lo:hi] = _bf16(blk, device)
+
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 4)) as ex:
+        list(ex.map(one, jobs))
+
+
 class DecodeWorkload:
     """One decode step for B sequences (CSA or HCA) on rotated cache copies."""
 
@@ -109,11 +126,12 @@ class DecodeWorkload:
         self.win = _bf16(np.stack([s.win for s in self.seqs]), device)
         self.kv_stage = _bf16(np.stack([s.kv_stage for s in self.seqs]), device)
         self.gate_stage = _bf16(np.stack([s.gate_stage for s in self.seqs]), device)
-        # caches: the first copy from the seeded generator, the others device copies
+        # caches: the first copy from the seeded generator (the visible rows of
+        # every sequence; rows past them are never read and stay zero), the
+        # others device copies
         self.copies = copies if cfg.ctx_lo == 0 else 1
-        kv0 = torch.empty((B, self.Ncap, D), dtype=torch.bfloat16, device=device)
-        for b in range(B):
-            kv0[b] = _bf16(synth.kv_cache_rows(cfg, b, self.Ncap), device)
+        kv0 = torch.zeros((B, self.Ncap, D), dtype=torch.bfloat16, device=device)
+        _fill_cache(kv0, cfg.cid, synth.T_KVCACHE, self.n_vis, device)
         self.kv = [kv0] + [kv0.clone() for _ in range(self.copies - 1)]
         self.out = torch.empty((B, 1, cfg.H, D), dtype=torch.float32, device=device)
         if cfg.csa:
@@ -121,9 +139,8 @@ class DecodeWorkload:
             self.w = _f32(np.stack([s.w for s in self.seqs])[:, None], device)
             self.ki_stage = _bf16(np.stack([s.ki_stage for s in self.seqs]), device)
             self.gi_stage = _bf16(np.stack([s.gi_stage for s in self.seqs]), device)
-            ic0 = torch.empty((B, self.Ncap, DI), dtype=torch.bfloat16, device=device)
-            for b in range(B):
-                ic0[b] = _bf16(synth.idx_cache_rows(cfg, b, self.Ncap), device)
+            ic0 = torch.zeros((B, self.Ncap, DI), dtype=torch.bfloat16, device=device)
+            _fill_cache(ic0, cfg.cid, synth.T_IDXCACHE, self.n_vis, device)
             self.idx_cache = [ic0] + [ic0.clone() for _ in range(self.copies - 1)]
             self.scores = torch.empty((B, 1, self.Ncap), dtype=torch.float32, device=device)
             self.sel = torch.empty((B, 1, cfg.k), dtype=torch.int32, device=device)

@@ -28,11 +28,22 @@ namespace {
 
 constexpr int kHI = 64;   // indexer heads on the matrix-core path
 constexpr int kDI = 128;  // indexer head dim on the matrix-core path
+constexpr int kRowB = kDI * 2;  // bytes per index row
 
 __device__ __forceinline__ int64_t visible_entries(const int* pos, int64_t qi, int ratio, int Ncap) {
   const int p = pos[qi];
   const int64_t nv = p >= 0 ? (int64_t(p) + 1) / ratio : 0;
   return nv < Ncap ? nv : Ncap;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+// One LDS copy instruction: lane l moves the 16 bytes at base + voff[l] to
+// LDS address lds + 16 l (M0 carries lds).  The kernel waits for it itself.
+__device__ __forceinline__ void copy_to_lds(const void* base, uint32_t voff, uint32_t lds) {
+  const uint64_t r = reinterpret_cast<uint64_t>(base);
+  const uint64_t su = uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(r)))) |
+                      (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(r >> 32)))) << 32);
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(su), "{m0}"(lds) : "memory");
 }
 
 // ---------------------------------------------------------------------------
@@ -158,18 +169,7 @@ constexpr int kTQ = 4;          // queries per workgroup (one per wave)
 constexpr int kTWaves = 4;
 constexpr int kTThreads = kTWaves * kWave;
 constexpr int kCR = 64;         // index rows per chunk
-constexpr int kRowB = kDI * 2;  // bytes per index row
 constexpr int kCopyPerWave = kCR / kTWaves / 4;  // 4 rows per LDS copy instruction
-
-typedef __attribute__((address_space(3))) void lds_void;
-// One LDS copy instruction: lane l moves the 16 bytes at base + voff[l] to
-// LDS address lds + 16 l (M0 carries lds).  The kernel waits for it itself.
-__device__ __forceinline__ void copy_to_lds(const void* base, uint32_t voff, uint32_t lds) {
-  const uint64_t r = reinterpret_cast<uint64_t>(base);
-  const uint64_t su = uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(r)))) |
-                      (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(r >> 32)))) << 32);
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(su), "{m0}"(lds) : "memory");
-}
 
 __global__ __launch_bounds__(kTThreads, 3) void index_tile(IndexArgs a, int groups_per_seq, int ngroups) {
   __shared__ __attribute__((aligned(16))) unsigned char rows[2][kCR * kRowB];
@@ -302,6 +302,117 @@ __global__ __launch_bounds__(kTThreads, 3) void index_tile(IndexArgs a, int grou
 }
 
 // ---------------------------------------------------------------------------
+// LDS-streaming kernel (few queries per sequence, e.g. decode): grid
+// (B*S, ceil(Ncap / (8*RW))), 8 waves, one workgroup per CU.  Wave w scores
+// rows [row0 + w*RW, row0 + (w+1)*RW) on its own, with no workgroup barrier
+// after the start: its rows come HBM -> LDS through a private four-slot ring
+// of 16-row chunks (each copy instruction moves 4 whole rows, 1 KiB
+// contiguous), three chunks copying while one is multiplied.  LDS rows are 256 B
+// with 16-byte chunk c of row r stored at chunk c ^ (r % 16).  Scores collect
+// in LDS and leave in 1 KiB stores at the end, so the copy waits never cover
+// a store.
+// ---------------------------------------------------------------------------
+constexpr int kDW = 8;        // waves per workgroup
+constexpr int kDChunk = 16;   // rows per ring slot
+constexpr int kDSlots = 4;    // ring slots per wave (kDSlots - 1 chunks in flight)
+constexpr int kDCopies = kDChunk / 4;  // copy instructions per chunk
+
+template <int RW>
+__global__ __launch_bounds__(kDW * kWave) void index_dma(IndexArgs a) {
+  static_assert(RW % kDChunk == 0 && RW >= kDChunk, "rows per wave");
+  __shared__ __attribute__((aligned(16))) unsigned char ring[kDW][kDSlots][kDChunk * kRowB];
+  __shared__ __attribute__((aligned(16))) float sc[kDW][RW];
+  __shared__ __attribute__((aligned(16))) float wsh[kHI];
+  const int64_t qi = blockIdx.x;
+  const int b = int(qi / a.S);
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int g = lane / 16, r16 = lane % 16;
+  const int Ncap = a.Ncap;
+  const int n_vis = int(visible_entries(a.pos, qi, a.ratio, Ncap));
+  const int row0 = int(blockIdx.y) * (kDW * RW);
+  float* srow = a.scores + qi * Ncap;
+  if (row0 >= n_vis) {  // nothing visible in this workgroup
+    for (int e = row0 + tid; e < row0 + kDW * RW && e < Ncap; e += kDW * kWave) srow[e] = -INFINITY;
+    return;
+  }
+  const int wr0 = row0 + wave * RW;  // this wave's first row
+  const int wr_vis = n_vis - wr0;    // visible rows from wr0 on (may be <= 0)
+  const int n_ch = wr_vis > 0 ? min(RW / kDChunk, (wr_vis + kDChunk - 1) / kDChunk) : 0;
+  const uint16_t* cache = static_cast<const uint16_t*>(a.cache) + int64_t(b) * Ncap * kDI;
+  const uint32_t ring_base = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)&ring[wave][0][0]));
+  // chunk ch of the wave: kDCopies copies of 4 rows; rows past the causal
+  // bound repeat the last visible row (finite, masked)
+  auto issue = [&](int ch) {
+#pragma unroll
+    for (int u = 0; u < kDCopies; ++u) {
+      const int rl = u * 4 + g;
+      const int e = min(wr0 + ch * kDChunk + rl, n_vis - 1);
+      const uint32_t voff = uint32_t(e) * kRowB + uint32_t(((r16 ^ (rl & 15)) << 4));
+      copy_to_lds(cache, voff, ring_base + uint32_t((ch % kDSlots) * kDChunk * kRowB + u * 4 * kRowB));
+    }
+  };
+#pragma unroll
+  for (int ch = 0; ch < kDSlots - 1; ++ch)
+    if (ch < n_ch) issue(ch);
+  if (tid < kHI) wsh[tid] = a.w[qi * kHI + tid];
+  bf16x8 qa[4][4];  // [head tile][K-step]: Q[mt*16 + r16][ks*32 + g*8 .. +7]
+  {
+    const uint4* q = reinterpret_cast<const uint4*>(a.q_idx) + qi * (kHI * kDI / 8);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qa[mt][ks] = as_bf16x8(q[(mt * 16 + r16) * (kDI / 8) + ks * 4 + g]);
+  }
+  __syncthreads();  // head weights
+  float wv[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[mt][i] = wsh[mt * 16 + g * 4 + i];
+  int koff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) koff[ks] = r16 * kRowB + (((ks * 4 + g) ^ r16) << 4);
+
+  for (int ch = 0; ch < n_ch; ++ch) {
+    // this wave's copies of chunk ch are done (later chunks may be in flight)
+    const int later = min(n_ch - 1 - ch, kDSlots - 2);
+    if (later >= 2) __builtin_amdgcn_s_waitcnt((2 * kDCopies) | (7 << 4) | (15 << 8));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(kDCopies | (7 << 4) | (15 << 8));
+    else __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    const unsigned char* tb = &ring[wave][ch % kDSlots][0];
+    {
+      bf16x8 kk[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kk[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(tb + koff[ks]));
+      floatx4 acc[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][0], kk[0], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+      for (int ks = 1; ks < 4; ++ks)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][ks], kk[ks], acc[mt], 0, 0, 0);
+      float p4[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        p4[mt] = relu(acc[mt][0]) * wv[mt][0] + relu(acc[mt][1]) * wv[mt][1] + relu(acc[mt][2]) * wv[mt][2] +
+                 relu(acc[mt][3]) * wv[mt][3];
+      const float part = sum_rows4((p4[0] + p4[1]) + (p4[2] + p4[3]));
+      const int rr = ch * kDChunk + r16;
+      if (g == 0) sc[wave][rr] = rr < wr_vis ? part : -INFINITY;
+    }
+    // the slot's rows are consumed (their reads returned before the MFMAs)
+    if (ch + kDSlots - 1 < n_ch) issue(ch + kDSlots - 1);
+  }
+  for (int rr = n_ch * kDChunk + lane; rr < RW; rr += kWave) sc[wave][rr] = -INFINITY;
+  // the wave's scores, 256 rows per 16-byte store instruction
+#pragma unroll
+  for (int r4 = lane * 4; r4 < RW; r4 += kWave * 4)
+    if (wr0 + r4 < Ncap) *reinterpret_cast<float4*>(srow + wr0 + r4) = *reinterpret_cast<const float4*>(&sc[wave][r4]);
+}
+
+// ---------------------------------------------------------------------------
 // Vector-ALU kernel for other shapes / fp32: one thread per (query, entry).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void index_any(IndexArgs a) {
@@ -337,13 +448,35 @@ hipError_t launch_index_score(const IndexArgs& a, hipStream_t stream) {
     const int gps = (a.S + kTQ - 1) / kTQ;
     const int ngroups = a.B * gps;
     hipLaunchKernelGGL(index_tile, dim3(unsigned(ngroups)), dim3(kTThreads), 0, stream, a, gps, ngroups);
+  } else if (a.use_mfma && a.H == kHI && a.D == kDI && a.Ncap % 4 == 0 && nq * int64_t(a.Ncap) >= (int64_t(1) << 21)) {
+    // long caches (>= 2M rows in all): rows per wave the smallest of 32 .. 512
+    // that keeps the grid within 2048 workgroups
+    const int64_t rows = nq * int64_t(a.Ncap);
+    int rw = 32;
+    while (rw < 512 && rows > int64_t(2048) * kDW * rw) rw *= 2;
+    const dim3 grid(unsigned(nq), unsigned((a.Ncap + kDW * rw - 1) / (kDW * rw)));
+    const dim3 block(kDW * kWave);
+    switch (rw) {
+      case 32: hipLaunchKernelGGL(index_dma<32>, grid, block, 0, stream, a); break;
+      case 64: hipLaunchKernelGGL(index_dma<64>, grid, block, 0, stream, a); break;
+      case 128: hipLaunchKernelGGL(index_dma<128>, grid, block, 0, stream, a); break;
+      case 256: hipLaunchKernelGGL(index_dma<256>, grid, block, 0, stream, a); break;
+      default: hipLaunchKernelGGL(index_dma<512>, grid, block, 0, stream, a); break;
+    }
   } else if (a.use_mfma && a.H == kHI && a.D == kDI) {
+    // one step per workgroup while that still gives few workgroups per CU;
+    // long caches run many steps per workgroup, so that fewer workgroups pay
+    // the start-up latency
     const int64_t blocks1 = nq * ((a.Ncap + kStepRows - 1) / kStepRows);
     if (blocks1 <= 4096) {
       const dim3 grid(unsigned(nq), (a.Ncap + kStepRows - 1) / kStepRows);
       hipLaunchKernelGGL(index_stream<1>, grid, dim3(kWave * kStreamWaves), 0, stream, a);
-    } else {
+    } else if (blocks1 <= 8192) {
       constexpr int kSteps = 4;
+      const dim3 grid(unsigned(nq), (a.Ncap + kStepRows * kSteps - 1) / (kStepRows * kSteps));
+      hipLaunchKernelGGL(index_stream<kSteps>, grid, dim3(kWave * kStreamWaves), 0, stream, a);
+    } else {
+      constexpr int kSteps = 16;
       const dim3 grid(unsigned(nq), (a.Ncap + kStepRows * kSteps - 1) / (kStepRows * kSteps));
       hipLaunchKernelGGL(index_stream<kSteps>, grid, dim3(kWave * kStreamWaves), 0, stream, a);
     }

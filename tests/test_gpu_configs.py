@@ -126,14 +126,15 @@ def test_hca_decode_1m():
 
 
 def test_csa_decode_1m_lengths_mix():
-    """The 1M-context CSA decode with per-sequence lengths U[512K, 1M]: the
-    first four sequences of the seeded draw (caches of 262,144 rows each)."""
+    """The 1M-context CSA decode with per-sequence lengths U[512K, 1M], all 32
+    sequences as the bench runs them (caches of 262,144 rows each); four
+    sequences are checked against the oracle."""
     import bench
-    wl = bench.DecodeWorkload(synth.CSA_DECODE_1M, "cuda", copies=1, batch=4)
-    assert len(set(int(n) for n in wl.lengths)) == 4
+    wl = bench.DecodeWorkload(synth.CSA_DECODE_1M, "cuda", copies=1)
+    assert len(set(int(n) for n in wl.lengths)) > 16
     progress("csa_decode_1m: step")
     _step(wl)
-    assert _check_decode(wl, [0, 1, 2, 3]) <= 1
+    assert _check_decode(wl, [0, 7, 19, 31]) <= 1
 
 
 def test_csa_prefill_8k():

@@ -154,6 +154,26 @@ def test_index_score_tile_path():
         assert_normwise(got[b], want, what=f"b={b}")
 
 
+def test_index_score_long_cache():
+    """Long caches (8 x 262,144 rows, the LDS-streaming decode kernel): full,
+    partial-wave, chunk-ragged, single-row and empty visibility."""
+    csa = csa_mod()
+    B, H, D, Ncap, r = 8, 64, 128, 262144, 4
+    n_vis = np.array([Ncap, 1, 0, 100000, 4096 * 3 + 17, 262143, 515, 4096], np.int64)
+    pos = np.where(n_vis > 0, n_vis * r + 1, -1).astype(np.int32).reshape(B, 1)
+    q = rows_bf16(27, (B, 1, H, D), unit=True)
+    k = rows_bf16(28, (B, Ncap, D), unit=True)
+    w = (np.random.default_rng(29).standard_normal((B, 1, H)) / math.sqrt(D) / math.sqrt(H)).astype(np.float32)
+    scores = torch.empty((B, 1, Ncap), device="cuda")
+    csa.csa_index_score(dev_bf16(q), dev(w), dev_bf16(k), dev(pos), scores, ratio=r)
+    got = scores.cpu().numpy()
+    for b in range(B):
+        nv = oracle.visible(int(pos[b, 0]), r) if pos[b, 0] >= 0 else 0
+        assert nv == min(n_vis[b], Ncap)
+        want = oracle.index_score(synth.bf16_to_f64(q[b, 0]), w[b, 0], synth.bf16_to_f64(k[b]), nv)
+        assert_normwise(got[b], want[None], what=f"b={b}")
+
+
 # ---------------------------------------------------------------------------
 # Top-k (identical float32 scores on both sides: bit-exact sets)
 # ---------------------------------------------------------------------------
