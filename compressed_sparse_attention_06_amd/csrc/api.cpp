@@ -139,12 +139,13 @@ int attn_common(const void* q, const void* cmp, int Ncap, const int* idx, int k,
   if (int64_t(B) * S > INT32_MAX) return CSA_ERR_UNSUPPORTED;
   const int64_t max_cand = int64_t(window) + (hca ? Ncap : k);
   if (max_cand > INT32_MAX) return CSA_ERR_UNSUPPORTED;
-  csa::AttnPlan plan = csa::plan_attn(B, S, H, D, int(max_cand), dtype, hca);
+  csa::AttnPlan plan = csa::plan_attn(B, S, H, D, window, hca ? Ncap : k, dtype, hca);
   if (plan.mfma && !(aligned16(q) && aligned16(cmp) && (window == 0 || aligned16(win)) && aligned16(out)))
-    plan = csa::AttnPlan{false, 1, 0, 0};
+    plan = csa::AttnPlan{false, false, 1, 0, 0};
   if (!plan.mfma && D > 1024) return CSA_ERR_UNSUPPORTED;
   if (plan.nsplit > kMaxGridY) return CSA_ERR_UNSUPPORTED;
   if (plan.ws_bytes > 0 && (ws == nullptr || ws_bytes < plan.ws_bytes)) return CSA_ERR_WORKSPACE;
+  if (plan.ws_bytes > 0 && !aligned16(ws)) return CSA_ERR_INVALID_ARG;
   csa::AttnArgs a{};
   a.q = q;
   a.cmp = cmp;
@@ -171,16 +172,16 @@ int attn_common(const void* q, const void* cmp, int Ncap, const int* idx, int k,
   return hip_status(csa::launch_attn(a, plan, hca, stream));
 }
 
-size_t attn_ws(int B, int S, int H, int D, int64_t max_cand, bool hca) {
-  if (B < 0 || S < 0 || H < 1 || D < 2 || max_cand < 0 || max_cand > INT32_MAX) return 0;
-  return csa::plan_attn(B, S, H, D, int(max_cand), CSA_BF16, hca).ws_bytes;
+size_t attn_ws(int B, int S, int H, int D, int window, int nsel, bool hca) {
+  if (B < 0 || S < 0 || H < 1 || D < 2 || window < 0 || nsel < 0 || int64_t(window) + nsel > INT32_MAX) return 0;
+  return csa::plan_attn(B, S, H, D, window, nsel, CSA_BF16, hca).ws_bytes;
 }
 
 }  // namespace
 
 size_t csa_sparse_attn_workspace_size(int B, int S, int H, int D, int k, int window) {
   if (k < 0 || window < 0) return 0;
-  return attn_ws(B, S, H, D, int64_t(window) + k, false);
+  return attn_ws(B, S, H, D, window, k, false);
 }
 
 int csa_sparse_attn(const void* q, const void* cmp, int Ncap, const int* idx, int k, const void* win, int Wcap,
@@ -193,7 +194,7 @@ int csa_sparse_attn(const void* q, const void* cmp, int Ncap, const int* idx, in
 
 size_t hca_attn_workspace_size(int B, int S, int H, int D, int Ncap, int window) {
   if (Ncap < 0 || window < 0) return 0;
-  return attn_ws(B, S, H, D, int64_t(window) + Ncap, true);
+  return attn_ws(B, S, H, D, window, Ncap, true);
 }
 
 int hca_attn(const void* q, const void* cmp, int Ncap, int ratio, const void* win, int Wcap, int window,

@@ -72,13 +72,17 @@ constexpr int kMaxSplits = 256;
 // bytes at row + voff to LDS address lds_row + 16 l (M0 carries lds_row).
 // Written as asm so that the compiler does not order LDS reads of other tile
 // buffers behind it; the kernel waits for these copies itself before the
-// barrier that publishes a tile.
+// barrier that publishes a tile.  The compiler's hazard checks do not see
+// into asm, so the asm supplies the wait states itself: a vector-memory
+// instruction must not read an SGPR that a VALU instruction (readlane,
+// readfirstlane) wrote fewer than 5 instructions before, and an M0 write
+// needs one wait state before an LDS-DMA load.
 __device__ __forceinline__ void copy_row_to_lds(const void* row, uint32_t voff, uint32_t lds_row) {
   // the row address is wave-uniform; readfirstlane states it so it can sit in SGPRs
   const uint64_t r = reinterpret_cast<uint64_t>(row);
   const uint64_t su = uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(r)))) |
                       (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(r >> 32)))) << 32);
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(su), "{m0}"(lds_row) : "memory");
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(su), "{m0}"(lds_row) : "memory");
 }
 // s_waitcnt with only the vector-memory count set (expcnt, lgkmcnt: no wait)
 template <int N>
@@ -509,14 +513,365 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int nsplit) {
 }
 
 // ---------------------------------------------------------------------------
-// Vector-ALU kernel for other shapes: one wave per (query, head), online
-// softmax over the candidates, D <= 1024.
+// Persistent matrix-core kernel for many queries without splits (prefill).
+// Grid G (about one workgroup per CU), 512 threads.  Workgroup x runs the
+// queries x, x + G, x + 2G, ... (at most kPMaxQ) as ONE stream of 32-row
+// tiles through the same warp-specialised pipeline as attn_mfma, so that row
+// copies and selection loads run ahead across query boundaries, the QK waves
+// load the next query's Q^T while the PV waves still work on the previous
+// query, and no query pays a pipeline fill or drain of its own.
+//   * PV waves issue every copy: wave 4+v copies rows 8v..8v+7 of each tile,
+//     and wave 4 also copies the next query's selection list into LDS when
+//     the copies enter a query (two list buffers, by query parity);
+//   * the QK waves start a query's sums at its first tile and hand them (and
+//     an overflow flag) to the PV waves at its last tile, by query parity;
+//   * the PV waves zero O at a query's first tile and normalise, rotate and
+//     store it in the step that consumes its last tile.
+// The sink reference of attn_mfma is kept; a query whose scores exceed it by
+// more than the headroom is flagged in redo[qi] and recomputed exactly by
+// attn_redo (never for ordinary data).
+// ---------------------------------------------------------------------------
+constexpr int kPMaxQ = 64;               // queries per workgroup
+constexpr int kPCopyRows = kT / 4;       // rows each PV wave copies per tile
+constexpr int kPMaxSel = 1024;           // CSA selections of a query staged in LDS
+constexpr int kPersistMinQueries = 512;  // fewer queries take attn_mfma
+constexpr int kEpiStores = 8 * 4;        // output stores per PV lane when a query ends (one per dim x head tile)
+
+// One selection-list copy HBM -> LDS: lane l moves the dword at base + voff to
+// LDS address lds + 4 l (wait states as in copy_row_to_lds).
+__device__ __forceinline__ void copy_dwords_to_lds(const void* base, uint32_t voff, uint32_t lds) {
+  const uint64_t r = reinterpret_cast<uint64_t>(base);
+  const uint64_t su = uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(r)))) |
+                      (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(r >> 32)))) << 32);
+  asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(su), "{m0}"(lds) : "memory");
+}
+
+template <bool HCA>
+__global__ __launch_bounds__(kThreads) void attn_persist(AttnArgs a, int* redo) {
+  __shared__ __attribute__((aligned(16))) unsigned char tiles[kBufs][kT * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t pt[2][kH * kPPitch];
+  __shared__ __attribute__((aligned(4))) uint8_t vmask[kBufs][4];  // [tile buffer][PV wave]: rows 8v + bit
+  __shared__ __attribute__((aligned(16))) int sel[2][HCA ? 1 : kPMaxSel];
+  __shared__ float lsum[2][2][kH];  // [query parity][QK row half][head]
+  __shared__ int ovf[2][4];         // [query parity][QK wave]
+  __shared__ int qpos[kPMaxQ];
+
+  const int G = gridDim.x;
+  const int x = blockIdx.x;
+  const int nq = a.B * a.S;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int g = lane / 16, c16 = lane % 16;
+  const int nqb = (nq - x + G - 1) / G;  // this workgroup's queries (x < nq, nqb <= kPMaxQ)
+  if (tid < nqb) qpos[tid] = a.pos[x + tid * G];
+  __syncthreads();
+
+  // candidate layout of the workgroup's query k
+  struct Query {
+    int k, qi, b, p, n_win, n_sel, s0, nt;
+  };
+  auto query = [&](int k) -> Query {
+    Query c;
+    c.k = k;
+    c.qi = x + k * G;
+    c.b = c.qi / a.S;
+    c.p = __builtin_amdgcn_readfirstlane(qpos[k]);
+    c.n_win = 0;
+    c.n_sel = 0;
+    c.s0 = 0;
+    if (c.p >= 0) {
+      c.n_win = c.p + 1 < a.window ? c.p + 1 : a.window;
+      c.s0 = int(uint32_t(c.p - c.n_win + 1) % uint32_t(a.Wcap));
+      if (HCA) {
+        const int nv = int((int64_t(c.p) + 1) / a.ratio);
+        c.n_sel = nv < a.Ncap ? nv : a.Ncap;
+      } else {
+        c.n_sel = a.k;
+      }
+    }
+    const int64_t n = int64_t(c.n_win) + c.n_sel;
+    c.nt = n > 0 ? int((n + kT - 1) / kT) : 1;  // a query with no candidates runs one masked tile
+    return c;
+  };
+  // a position in the stream: tile t of query c
+  struct Cur {
+    Query c;
+    int t;
+  };
+  auto advance = [&](Cur& u) {
+    if (++u.t == u.c.nt) {
+      u.t = 0;
+      if (u.c.k + 1 < nqb) u.c = query(u.c.k + 1);
+      else u.c.k = nqb;
+    }
+  };
+  int total = 0;
+  for (int k = 0; k < nqb; ++k) total += query(k).nt;
+  const Cur first{query(0), 0};
+
+  const uint32_t lds_tiles = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)&tiles[0][0]));
+  const uint32_t lds_sel = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)&sel[0][0]));
+  const int pw = wave - 4;  // PV wave index (copies)
+  // selection list of query k -> sel[k & 1] (wave 4 only)
+  auto copy_sel = [&](int k) {
+    const int* src = a.idx + int64_t(x + k * G) * a.k;
+    const uint32_t dst = lds_sel + uint32_t((k & 1) * kPMaxSel * 4);
+    for (int m = 0; m * kWave < a.k; ++m) {
+      const int i = m * kWave + lane;
+      copy_dwords_to_lds(src, uint32_t(i < a.k ? i : 0) * 4u, dst + uint32_t(m * kWave * 4));
+    }
+  };
+  // copies of stream tile u (tile u.t of query u.c) into buffer u % kBufs
+  auto issue = [&](const Cur& cu, int u) {
+    if (!HCA && pw == 0 && cu.t == 0 && cu.c.k + 1 < nqb) copy_sel(cu.c.k + 1);  // lands before cu's next query
+    const int buf = u % kBufs;
+    const int j = cu.t * kT + pw * kPCopyRows + (lane % kPCopyRows);
+    int code = -1;  // >= 0 compressed entry, <= -2 window ring slot, -1 none
+    if (j < cu.c.n_win) {
+      const int slot = cu.c.s0 + j;
+      code = -2 - (slot >= a.Wcap ? slot - a.Wcap : slot);
+    } else if (j - cu.c.n_win < cu.c.n_sel) {
+      const int i = j - cu.c.n_win;
+      if (HCA) {
+        code = i;
+      } else {
+        const int e = sel[cu.c.k & 1][i];
+        code = (e >= 0 && e < a.Ncap) ? e : -1;
+      }
+    }
+    const uint64_t ok = __ballot(code != -1);
+    if (lane == 0) vmask[buf][pw] = uint8_t(ok & 0xffu);
+    const uint16_t* win = static_cast<const uint16_t*>(a.win) + int64_t(cu.c.b) * a.Wcap * kD;
+    const uint16_t* cmp = static_cast<const uint16_t*>(a.cmp) + int64_t(cu.c.b) * a.Ncap * kD;
+    // the query's first head row stands in for a missing candidate (masked, finite)
+    const uint16_t* filler = static_cast<const uint16_t*>(a.q) + int64_t(cu.c.qi) * kH * kD;
+    const uint32_t dst = lds_tiles + uint32_t(buf * kT * kPitch + pw * kPCopyRows * kPitch);
+    // rows 8v..8v+3 are flipped iff v is odd, rows 8v+4..8v+7 iff v is even
+    const uint32_t voff_lo = uint32_t(lane ^ ((pw & 1) << 3)) * 16u;
+    const uint32_t voff_hi = uint32_t(lane ^ (((pw & 1) ^ 1) << 3)) * 16u;
+    // lane r forms row r's address; each copy reads it back as a scalar pair
+    const uint16_t* src = code >= 0 ? cmp + int64_t(code) * kD : (code <= -2 ? win + int64_t(-2 - code) * kD : filler);
+    const uint64_t sa = reinterpret_cast<uint64_t>(src);
+#pragma unroll
+    for (int r = 0; r < kPCopyRows; ++r) {
+      const uint64_t ra = uint64_t(uint32_t(__builtin_amdgcn_readlane(uint32_t(sa), r))) |
+                          (uint64_t(uint32_t(__builtin_amdgcn_readlane(uint32_t(sa >> 32), r))) << 32);
+      copy_row_to_lds(reinterpret_cast<const void*>(ra), r < 4 ? voff_lo : voff_hi, dst + uint32_t(r * kPitch));
+    }
+  };
+  const float qk_scale = a.scale * kLog2e;
+
+  if (wave < 4) {
+    // ===================== QK waves =====================
+    const int hh = wave & 1, rr = wave >> 1;
+    bf16x8 qb[2][16];
+    auto load_q = [&](int qi) {
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) {
+        const uint16_t* q =
+            static_cast<const uint16_t*>(a.q) + (int64_t(qi) * kH + hh * 32 + ht * 16 + c16) * kD + g * 8;
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) qb[ht][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(q + ks * 32));
+      }
+    };
+    load_q(first.c.qi);
+    __syncthreads();  // prologue: first selection list
+    __syncthreads();  // prologue: second selection list
+    const int k_base = (rr * 16 + c16) * kPitch + g * 16;
+    const int k_off0 = k_base + row_flip(c16) * 128, k_off1 = k_base - row_flip(c16) * 128;
+    float m_ref[2], l_sink[2];
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      const int h = hh * 32 + ht * 16 + c16;
+      m_ref[ht] = sink_ref(a.sink, h);
+      l_sink[ht] = (rr == 0 && g == 0) ? fast_exp2(a.sink[h] * kLog2e - m_ref[ht]) : 0.f;
+    }
+    float l_run[2] = {0.f, 0.f}, m_run[2] = {-INFINITY, -INFINITY};
+    bool over = false;
+    Cur cq = first;
+    for (int s = 0; s <= total; ++s) {
+      __syncthreads();
+      if (s == total) break;
+      if (cq.t == 0) {
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+          l_run[ht] = l_sink[ht];
+          m_run[ht] = -INFINITY;
+        }
+        over = false;
+      }
+      const unsigned char* tile = tiles[s % kBufs];
+      const uint32_t okm = *reinterpret_cast<const uint16_t*>(&vmask[s % kBufs][rr * 2]);  // rows rr*16 + bit
+      floatx4 st[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+      bf16x8 kr[kAheadK + 1];
+#pragma unroll
+      for (int ks = 0; ks < kAheadK; ++ks)
+        kr[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(tile + ((ks & 2) ? k_off1 : k_off0) + ks * 64));
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        if (ks + kAheadK < 16)
+          kr[(ks + kAheadK) % (kAheadK + 1)] = as_bf16x8(*reinterpret_cast<const uint4*>(
+              tile + (((ks + kAheadK) & 2) ? k_off1 : k_off0) + (ks + kAheadK) * 64));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht)
+          st[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[ks % (kAheadK + 1)], qb[ht][ks], st[ht], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const bool last = cq.t == cq.c.nt - 1;
+      if (last && cq.c.k + 1 < nqb) load_q(cq.c.qi + G);  // the next query's Q^T lands during this step
+      uint16_t* pw_t = &pt[s & 1][0];
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) {
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool ok = (okm >> (4 * g + i)) & 1u;
+          const float sv = ok ? st[ht][i] * qk_scale : -INFINITY;
+          m_run[ht] = fmaxf(m_run[ht], sv);
+          p[i] = fast_exp2(sv - m_ref[ht]);
+        }
+        over = over || (m_run[ht] > m_ref[ht] + kHeadroom);
+        l_run[ht] += (p[0] + p[1]) + (p[2] + p[3]);
+        *reinterpret_cast<uint2*>(&pw_t[(hh * 32 + ht * 16 + c16) * kPPitch + rr * 16 + g * 4]) =
+            uint2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+      }
+      if (last) {
+        const int par = cq.c.k & 1;
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+          const float l = sum_rows4(l_run[ht]);
+          if (g == 0) lsum[par][rr][hh * 32 + ht * 16 + c16] = l;
+        }
+        const bool any_over = __any(over);
+        if (lane == 0) ovf[par][wave] = any_over ? 1 : 0;
+      }
+      advance(cq);
+    }
+  } else {
+    // ===================== PV waves =====================
+    // prologue: query 0's selection list, then tiles 0 and 1 (tile 0 copies
+    // query 1's list first)
+    Cur ci = first;
+    if (!HCA && pw == 0) copy_sel(0);
+    wait_vmem<0>();
+    __syncthreads();
+    issue(ci, 0);
+    advance(ci);
+    wait_vmem<kPCopyRows>();  // query 1's list has landed, tile 0 may still be in flight
+    __syncthreads();
+    if (total > 1) {
+      issue(ci, 1);
+      advance(ci);
+    }
+    const int v_base = (g * 8 + (c16 >> 2)) * kPitch + pw * 256 + (((c16 >> 1) & 1) << 4) + ((c16 & 1) << 3);
+    const int f_lo = (g & 1) * 128, f_hi = ((g & 1) ^ 1) * 128;
+    const int v_lo0 = v_base + f_lo, v_lo1 = v_base - f_lo;
+    const int v_hi0 = v_base + 4 * kPitch + f_hi, v_hi1 = v_base + 4 * kPitch - f_hi;
+    const int rope0 = kD - a.rope_dim;
+    floatx4 acc[8][4];
+    Cur cp = first;
+    bool stored = false;  // the previous step stored a query's output (kEpiStores stores per lane)
+    for (int s = 0; s <= total; ++s) {
+      // tile s has landed; only tile s+1's copies and the output stores that
+      // followed them may still be in flight
+      if (s + 1 < total) {
+        if (stored) wait_vmem<kPCopyRows + kEpiStores>();
+        else wait_vmem<kPCopyRows>();
+      } else {
+        wait_vmem<0>();
+      }
+      __syncthreads();
+      stored = false;
+      if (s + 2 < total) {
+        issue(ci, s + 2);
+        advance(ci);
+      }
+      if (s == 0) continue;
+      if (cp.t == 0) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+          for (int ht = 0; ht < 4; ++ht) acc[dt][ht] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+      const unsigned char* tile = tiles[(s - 1) % kBufs];
+      const uint16_t* pr = &pt[(s - 1) & 1][0];
+      bf16x8 pb[4];
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht)
+        pb[ht] = as_bf16x8(*reinterpret_cast<const uint4*>(&pr[(ht * 16 + c16) * kPPitch + g * 8]));
+      bf16x8 vr[kAheadV + 1];
+      auto vload = [&](int dt, bf16x8& dst) {
+        const uint2 lo = lds_read_tr16(tile + ((dt & 4) ? v_lo1 : v_lo0) + dt * 32);
+        const uint2 hi = lds_read_tr16(tile + ((dt & 4) ? v_hi1 : v_hi0) + dt * 32);
+        dst = as_bf16x8(uint4{lo.x, lo.y, hi.x, hi.y});
+      };
+#pragma unroll
+      for (int dt = 0; dt < kAheadV; ++dt) vload(dt, vr[dt]);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        if (dt + kAheadV < 8) vload(dt + kAheadV, vr[(dt + kAheadV) % (kAheadV + 1)]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht)
+          acc[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr[dt % (kAheadV + 1)], pb[ht], acc[dt][ht], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (cp.t == cp.c.nt - 1) {
+        // the query's last tile: O / sum, inverse RoPE, store
+        const int par = cp.c.k & 1;
+        const int p = cp.c.p;
+        float inv_l[4];
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) inv_l[ht] = 1.f / (lsum[par][0][ht * 16 + c16] + lsum[par][1][ht * 16 + c16]);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const int d0 = pw * 128 + dt * 16 + g * 4;
+          float cs[2] = {1.f, 1.f}, sn[2] = {0.f, 0.f};
+          const bool rot = d0 >= rope0 && p >= 0;
+          if (rot) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) rope_cos_sin(p, (d0 + 2 * u - rope0) / 2, a.rope_dim, a.rope_base, &cs[u], &sn[u]);
+          }
+#pragma unroll
+          for (int ht = 0; ht < 4; ++ht) {
+            float o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = acc[dt][ht][i] * inv_l[ht];
+            if (rot) {
+#pragma unroll
+              for (int u = 0; u < 2; ++u) {
+                const float x0 = o[2 * u], x1 = o[2 * u + 1];
+                o[2 * u] = x0 * cs[u] + x1 * sn[u];
+                o[2 * u + 1] = x1 * cs[u] - x0 * sn[u];
+              }
+            }
+            const int64_t off = (int64_t(cp.c.qi) * kH + ht * 16 + c16) * kD + d0;
+            if (a.out_dtype == CSA_BF16) {
+              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + off) =
+                  uint2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+            } else {
+              *reinterpret_cast<float4*>(static_cast<float*>(a.out) + off) = float4{o[0], o[1], o[2], o[3]};
+            }
+          }
+        }
+        if (pw == 0 && lane == 0) redo[cp.c.qi] = (ovf[par][0] | ovf[par][1] | ovf[par][2] | ovf[par][3]) ? 1 : 0;
+        stored = true;
+      }
+      advance(cp);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Vector-ALU path for other shapes: one wave per (query, head), online
+// softmax over the candidates with the exact running maximum, D <= 1024.
 // ---------------------------------------------------------------------------
 template <bool HCA>
-__global__ __launch_bounds__(kWave) void attn_any(AttnArgs a) {
-  extern __shared__ float obuf[];  // D floats
-  const int64_t qi = blockIdx.x;
-  const int h = blockIdx.y, lane = threadIdx.x;
+// (a is taken by value: a reference to the kernel argument made the compiler
+// spill the row pointers to the stack and load rows through flat addresses)
+__device__ __forceinline__ void attn_head(const AttnArgs a, int64_t qi, int h, float* obuf) {
+  const int lane = threadIdx.x;
   const int b = int(qi / a.S);
   const int D = a.D;
   const Cand c = candidates(a, HCA, qi);
@@ -571,14 +926,40 @@ __global__ __launch_bounds__(kWave) void attn_any(AttnArgs a) {
   }
   __syncthreads();
   for (int d = lane; d < D; d += kWave) store_elem(a.out, a.out_dtype, qoff + d, obuf[d]);
+  __syncthreads();  // obuf is free for the next head
+}
+
+// grid (B*S, H), one wave
+template <bool HCA>
+__global__ __launch_bounds__(kWave) void attn_any(AttnArgs a) {
+  extern __shared__ float obuf[];  // D floats
+  attn_head<HCA>(a, blockIdx.x, blockIdx.y, obuf);
+}
+
+// Recompute, exactly, the queries the persistent kernel flagged (redo[qi] != 0):
+// grid (ceil(B*S / 64), H), one wave; each wave checks 64 flags with one load
+// and recomputes its head of the flagged ones.
+template <bool HCA>
+__global__ __launch_bounds__(kWave) void attn_redo(AttnArgs a, const int* redo) {
+  extern __shared__ float obuf[];
+  const int64_t nq = int64_t(a.B) * a.S;
+  const int64_t q0 = int64_t(blockIdx.x) * kWave;
+  const int64_t mine = q0 + threadIdx.x;
+  uint64_t todo = __ballot(mine < nq && redo[mine] != 0);
+  while (todo != 0) {
+    const int l = __builtin_ctzll(todo);
+    todo &= todo - 1;
+    attn_head<HCA>(a, q0 + l, blockIdx.y, obuf);
+  }
 }
 
 }  // namespace
 
-AttnPlan plan_attn(int B, int S, int H, int D, int max_cand, int dtype, bool hca) {
-  AttnPlan p{false, 1, 0, 0};
+AttnPlan plan_attn(int B, int S, int H, int D, int window, int nsel, int dtype, bool hca) {
+  AttnPlan p{false, false, 1, 0, 0};
   p.mfma = dtype == CSA_BF16 && H == kH && D == kD;
   if (!p.mfma) return p;
+  const int64_t max_cand = int64_t(window) + nsel;
   const int64_t nq = int64_t(B) * S;
   int64_t want = nq > 0 ? (kTargetBlocks + nq - 1) / nq : 1;
   const int64_t most = (max_cand + kMinSplitRows - 1) / kMinSplitRows;
@@ -593,18 +974,35 @@ AttnPlan plan_attn(int B, int S, int H, int D, int max_cand, int dtype, bool hca
   p.nsplit = int((max_cand + rows - 1) / rows);
   if (p.nsplit < 1) p.nsplit = 1;
   if (p.nsplit > kMaxSplits) {  // more CSA candidates than the split table holds
-    p = AttnPlan{false, 1, 0, 0};
+    p = AttnPlan{false, false, 1, 0, 0};
     return p;
   }
-  if (p.nsplit > 1)
+  if (p.nsplit > 1) {
     p.ws_bytes = size_t(nq) * p.nsplit * kH * (size_t(kD) + 2) * sizeof(float);
+  } else if (nq >= kPersistMinQueries && (hca || nsel <= kPMaxSel)) {
+    p.persist = true;
+    p.ws_bytes = size_t(nq) * sizeof(int);  // per-query recompute flags
+  }
   return p;
 }
 
 hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, bool hca, hipStream_t stream) {
   const int64_t nq = int64_t(a.B) * a.S;
   if (nq == 0) return hipSuccess;
-  if (plan.mfma) {
+  if (plan.persist) {
+    int64_t G = (nq + kPMaxQ - 1) / kPMaxQ;
+    if (G < kTargetBlocks) G = kTargetBlocks;
+    if (G > nq) G = nq;
+    int* redo = static_cast<int*>(a.ws);
+    const dim3 redo_grid(unsigned((nq + kWave - 1) / kWave), a.H);
+    if (hca) {
+      hipLaunchKernelGGL((attn_persist<true>), dim3(unsigned(G)), dim3(kThreads), 0, stream, a, redo);
+      hipLaunchKernelGGL((attn_redo<true>), redo_grid, dim3(kWave), a.D * sizeof(float), stream, a, redo);
+    } else {
+      hipLaunchKernelGGL((attn_persist<false>), dim3(unsigned(G)), dim3(kThreads), 0, stream, a, redo);
+      hipLaunchKernelGGL((attn_redo<false>), redo_grid, dim3(kWave), a.D * sizeof(float), stream, a, redo);
+    }
+  } else if (plan.mfma) {
     const dim3 grid(unsigned(nq), plan.nsplit);
     const bool split = plan.nsplit > 1;
     if (hca && split) hipLaunchKernelGGL((attn_mfma<true, true>), grid, dim3(kThreads), 0, stream, a, plan.nsplit, plan.chunk_rows);

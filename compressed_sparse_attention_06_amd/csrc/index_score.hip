@@ -39,11 +39,14 @@ __device__ __forceinline__ int64_t visible_entries(const int* pos, int64_t qi, i
 typedef __attribute__((address_space(3))) void lds_void;
 // One LDS copy instruction: lane l moves the 16 bytes at base + voff[l] to
 // LDS address lds + 16 l (M0 carries lds).  The kernel waits for it itself.
+// The asm supplies its own wait states (the compiler's hazard checks do not
+// see into asm): 5 after a VALU write of the address SGPRs, 1 after the M0
+// write.
 __device__ __forceinline__ void copy_to_lds(const void* base, uint32_t voff, uint32_t lds) {
   const uint64_t r = reinterpret_cast<uint64_t>(base);
   const uint64_t su = uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(r)))) |
                       (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(r >> 32)))) << 32);
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(su), "{m0}"(lds) : "memory");
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(su), "{m0}"(lds) : "memory");
 }
 
 // ---------------------------------------------------------------------------

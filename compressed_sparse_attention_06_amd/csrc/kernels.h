@@ -71,11 +71,12 @@ struct AttnArgs {
 };
 struct AttnPlan {
   bool mfma;
+  bool persist;  // one persistent workgroup per CU streams many queries
   int nsplit;
   int chunk_rows;
   size_t ws_bytes;
 };
-AttnPlan plan_attn(int B, int S, int H, int D, int max_cand, int dtype, bool hca);
+AttnPlan plan_attn(int B, int S, int H, int D, int window, int nsel, int dtype, bool hca);
 hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, bool hca, hipStream_t stream);
 
 }  // namespace csa

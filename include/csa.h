@@ -163,7 +163,11 @@ int csa_topk(const float* scores, const int* n_valid, int R, int N, int k, int* 
  *   out [B,S,H,D] (out_dtype).  A prefill passes its per-token window rows
  *   with Wcap >= the largest position + 1.
  * Matrix-core path: dtype CSA_BF16, H == 64, D == 512.  Other shapes run a
- * vector-ALU path (D <= 1024).  ws: csa_sparse_attn_workspace_size bytes.
+ * vector-ALU path (D <= 1024).  ws: csa_sparse_attn_workspace_size bytes,
+ * 16-byte aligned, caller-owned (device memory; may be null when the size
+ * is 0): split partials for few queries, one recompute flag per query for
+ * many.  Returns CSA_ERR_WORKSPACE when too small, CSA_ERR_INVALID_ARG when
+ * misaligned.
  */
 size_t csa_sparse_attn_workspace_size(int B, int S, int H, int D, int k, int window);
 int csa_sparse_attn(const void* q, const void* cmp, int Ncap, const int* idx, int k,
@@ -179,7 +183,7 @@ int csa_sparse_attn(const void* q, const void* cmp, int Ncap, const int* idx, in
  * [V4-Flash walkthrough] "长上下文时，先数真正访问的条目": its read count
  * grows with the context.  Same as csa_sparse_attn with the selection
  * replaced by entries 0 .. n_vis-1, n_vis = min((pos+1)/ratio, Ncap).
- * ws: hca_attn_workspace_size bytes.
+ * ws: hca_attn_workspace_size bytes (as for csa_sparse_attn).
  */
 size_t hca_attn_workspace_size(int B, int S, int H, int D, int Ncap, int window);
 int hca_attn(const void* q, const void* cmp, int Ncap, int ratio,

@@ -125,7 +125,10 @@ def test_sparse_attn_rejects(lib, bad):
 def test_attn_workspace_sizes(lib):
     ws = lib.csa_sparse_attn_workspace_size(8, 1, 64, 512, 512, 128)
     assert ws > 0 and ws % (64 * 514 * 4 * 8) == 0       # whole (query, split, head) partials
-    assert lib.csa_sparse_attn_workspace_size(1, 8192, 64, 512, 512, 128) == 0  # one split per query
+    # many queries: one persistent pass, one recompute flag per query
+    assert lib.csa_sparse_attn_workspace_size(1, 8192, 64, 512, 512, 128) == 8192 * 4
+    assert lib.csa_sparse_attn_workspace_size(1, 300, 64, 512, 512, 128) == 0  # one split per query
+    assert lib.hca_attn_workspace_size(2, 4096, 64, 512, 64, 128) == 2 * 4096 * 4
     assert _attn(lib, ws=None, ws_bytes=0) == WORKSPACE
     assert _attn(lib, ws_bytes=ws - 1) == WORKSPACE
     assert _attn(lib, dtype=0, D=2048, H=64, rope_dim=64) == UNSUPPORTED

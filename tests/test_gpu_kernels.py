@@ -217,12 +217,15 @@ def _attn_case(B, S, Ncap, k, window, Wcap, pos, seed, H=64, D=512, rope=64):
     return q, cmp, win, sink, sel
 
 
-def _oracle_attn(q, cmp, win, sink, sel, pos, window, Wcap, scale, rope, hca_ratio=None):
+def _oracle_attn(q, cmp, win, sink, sel, pos, window, Wcap, scale, rope, hca_ratio=None, only=None):
+    """Oracle attention of every query, or of the (b, s) pairs in `only`."""
     B, S = pos.shape
     out = np.zeros(q.shape)
     for b in range(B):
         cmpb = synth.bf16_to_f64(cmp[b])
         for s in range(S):
+            if only is not None and (b, s) not in only:
+                continue
             p = int(pos[b, s])
             wr = [synth.bf16_to_f64(win[b, pp % Wcap]) for pp in oracle.window_positions(p, window)] if p >= 0 else []
             wr = np.stack(wr) if wr else np.zeros((0, cmp.shape[-1]))
@@ -269,6 +272,71 @@ def test_hca_attn_mfma():
     csa.hca_attn(dev_bf16(q), dev_bf16(cmp), dev_bf16(win), dev(pos), dev(sink), out, ratio=r, window=window,
                  scale=scale, rope_dim=64)
     assert_attn(host(out), want, what="hca")
+
+
+def _scaled_bf16(bits, factor):
+    return synth.bf16_bits((synth.bf16_to_f32(bits) * factor).astype(np.float32))
+
+
+@pytest.mark.parametrize("hca", [False, True])
+def test_attn_persistent_stream(hca):
+    """Many queries: one persistent workgroup per CU streams 4-5 queries of
+    mixed lengths (no candidates, a partial window, a full window plus
+    selections) back to back; every query is compared."""
+    csa = csa_mod()
+    B, S, Ncap, k, window, Wcap, D, r = 2, 600, 2048, 512, 128, 8192, 512, 16
+    pos = np.stack([np.arange(S) + 7000, np.arange(S)]).astype(np.int32)
+    pos[0, 5:12] = [-1, 0, 1, 127, 128, 129, 3]
+    pos[1, 590:] = -1
+    q, cmp, win, sink, sel = _attn_case(B, S, Ncap, k, window, Wcap, pos, 61)
+    scale = 1 / math.sqrt(D)
+    assert csa.csa_sparse_attn_workspace_size(B, S, 64, D, k, window) == B * S * 4
+    want = _oracle_attn(q, cmp, win, sink, None if hca else sel, pos, window, Wcap, scale, 64,
+                        hca_ratio=r if hca else None)
+    out = torch.empty((B, S, 64, D), device="cuda", dtype=torch.bfloat16)
+    if hca:
+        csa.hca_attn(dev_bf16(q), dev_bf16(cmp), dev_bf16(win), dev(pos), dev(sink), out, ratio=r, window=window,
+                     scale=scale, rope_dim=64)
+    else:
+        csa.csa_sparse_attn(dev_bf16(q), dev_bf16(cmp), dev(sel), dev_bf16(win), dev(pos), dev(sink), out,
+                            window=window, scale=scale, rope_dim=64)
+    assert_attn(host(out), want, what="hca persistent" if hca else "csa persistent")
+
+
+@pytest.mark.parametrize("kind", ["csa_many", "hca_many", "csa_split"])
+def test_attn_score_overflow(kind):
+    """Scores far above the sink (beyond the fixed reference's headroom): the
+    split kernel repeats its pass with the true maximum, and the persistent
+    kernel flags the query for the exact recompute."""
+    csa = csa_mod()
+    Ncap, k, window, D, r = 2048, 512, 128, 512, 16
+    if kind == "csa_split":
+        B, S, Wcap = 2, 1, 128
+        pos = np.array([[8191], [300]], np.int32)
+    else:
+        B, S, Wcap = 1, 640, 8192
+        pos = (np.arange(S) + 5000).astype(np.int32)[None]
+    q, cmp, win, sink, sel = _attn_case(B, S, Ncap, k, window, Wcap, pos, 71)
+    # hot queries: logits spread 30x wider than usual, the largest ~100 above the sink
+    hot = [(B - 1, s) for s in range(S) if s % 5 == 2 or S == 1]
+    for b, s in hot:
+        q[b, s] = _scaled_bf16(q[b, s], 30.0)
+    cold = [(0, s) for s in range(0, S, 37)]
+    only = set(hot) | set(cold)
+    scale = 1 / math.sqrt(D)
+    hca = kind == "hca_many"
+    want = _oracle_attn(q, cmp, win, sink, None if hca else sel, pos, window, Wcap, scale, 64,
+                        hca_ratio=r if hca else None, only=only)
+    out = torch.empty((B, S, 64, D), device="cuda")
+    if hca:
+        csa.hca_attn(dev_bf16(q), dev_bf16(cmp), dev_bf16(win), dev(pos), dev(sink), out, ratio=r, window=window,
+                     scale=scale, rope_dim=64)
+    else:
+        csa.csa_sparse_attn(dev_bf16(q), dev_bf16(cmp), dev(sel), dev_bf16(win), dev(pos), dev(sink), out,
+                            window=window, scale=scale, rope_dim=64)
+    got = host(out)
+    ids = sorted(only)
+    assert_attn(np.stack([got[b, s] for b, s in ids]), np.stack([want[b, s] for b, s in ids]), what=kind)
 
 
 def test_attn_vector_path_fp32():
