@@ -88,7 +88,8 @@ int csa_index_score(const void* q_idx, const float* w, const void* idx_cache, in
   if (!q_idx || !w || !idx_cache || !pos || !scores) return CSA_ERR_INVALID_ARG;
   if (!dtype_ok(dtype) || B < 0 || S < 0 || H_I < 1 || D_I < 1 || Ncap < 0 || ratio < 1) return CSA_ERR_INVALID_ARG;
   if (int64_t(B) * S > INT32_MAX || (int64_t(Ncap) + 255) / 256 > kMaxGridY) return CSA_ERR_UNSUPPORTED;
-  const bool mfma = dtype == CSA_BF16 && H_I == 64 && D_I == 128 && aligned16(q_idx) && aligned16(idx_cache);
+  const bool mfma = dtype == CSA_BF16 && H_I == 64 && D_I == 128 && aligned16(q_idx) && aligned16(idx_cache) &&
+                    aligned16(scores);  // the matrix-core kernels store scores in 16-byte groups
   if (!mfma && int64_t(H_I) * D_I + H_I > 16384) return CSA_ERR_UNSUPPORTED;
   csa::IndexArgs a{};
   a.q_idx = q_idx;

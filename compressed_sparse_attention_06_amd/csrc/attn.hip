@@ -164,6 +164,18 @@ __device__ __forceinline__ int cand_code(const AttnArgs& a, bool hca, const Cand
   return (e >= 0 && e < a.Ncap) ? int(e) : -1;
 }
 
+// Split partials.  Split (qi, split) stores its unnormalised O (64 heads x 512
+// dims, fp32) in 128 blocks of 1 KiB, block (v, dt, ht) holding, at lane l's
+// 16 bytes, dims 128v + 16dt + 4(l/16) + 0..3 of head 16ht + l%16 -- the PV
+// waves' accumulator fragments, so that both the stores and the combine's
+// loads are whole contiguous blocks.  After all partials: (reference, sum)
+// per (qi, split, head) in fp32.
+constexpr int kPartialVecs = kH * kD * 4 / 16;  // 16-byte units per split partial
+__device__ __forceinline__ int partial_block(int v, int dt, int ht) { return (v * 8 + dt) * 4 + ht; }
+__device__ __forceinline__ float* partial_ml(const AttnArgs& a, int nsplit) {
+  return reinterpret_cast<float*>(static_cast<char*>(a.ws) + size_t(a.B) * a.S * nsplit * kPartialVecs * 16);
+}
+
 // ---------------------------------------------------------------------------
 // Matrix-core kernel: grid (B*S, nsplit), 512 threads (8 waves), one
 // workgroup per CU.
@@ -224,13 +236,22 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
       copy_row_to_lds(src, voff, dst + uint32_t(u * kPitch));
     }
   };
-  // top of tile step s: tile s has landed (only tile s+1's copies may still
-  // be in flight), then the barrier publishes it and frees tile s-2's buffer
+  // The first min(n_tiles, kBufs) tiles are copied up front (every buffer is
+  // free then); afterwards step s copies tile s+2 into the buffer that tile
+  // s-2 left.  Top of step s: tile s has landed (only later tiles' copies may
+  // be in flight), then the barrier publishes it.
+  auto prologue = [&]() {
+    for (int t = 0; t < n_tiles && t < kBufs; ++t) issue(t);
+  };
   auto step_sync = [&](int s) {
-    if (s + 1 < n_tiles) wait_vmem<kCopyRows>();
+    const int hi = s + 2 > kBufs ? s + 2 : kBufs;
+    const int later = (n_tiles < hi ? n_tiles : hi) - (s + 1);  // tiles issued after tile s
+    if (later >= 3) wait_vmem<3 * kCopyRows>();
+    else if (later == 2) wait_vmem<2 * kCopyRows>();
+    else if (later == 1) wait_vmem<kCopyRows>();
     else wait_vmem<0>();
     __syncthreads();
-    if (s + 2 < n_tiles) issue(s + 2);
+    if (s + 2 >= kBufs && s + 2 < n_tiles) issue(s + 2);
   };
   const float qk_scale = a.scale * kLog2e;
 
@@ -260,8 +281,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
         l_run[ht] = (!SPLIT && rr == 0 && g == 0) ? fast_exp2(s2 - m_ref[ht]) : 0.f;
         m_run[ht] = -INFINITY;
       }
-      if (n_tiles > 0) issue(0);
-      if (n_tiles > 1) issue(1);
+      prologue();
       for (int s = 0; s <= n_tiles; ++s) {
         step_sync(s);
         if (s == n_tiles) break;
@@ -342,8 +362,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
       for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) acc[dt][ht] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (n_tiles > 0) issue(0);
-      if (n_tiles > 1) issue(1);
+      prologue();
       for (int s = 0; s <= n_tiles; ++s) {
         step_sync(s);
         if (s == 0) continue;
@@ -413,19 +432,19 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
         }
       }
     } else {
-      float* ws_o = static_cast<float*>(a.ws);
-      const int64_t slot0 = (qi * nsplit + split) * kH;
+      // unnormalised partial O in fragment order: every store is one
+      // contiguous 1 KiB block (see partial_block)
+      floatx4* ws_o = static_cast<floatx4*>(a.ws) + (qi * nsplit + split) * kPartialVecs;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht)
-          *reinterpret_cast<floatx4*>(ws_o + (slot0 + ht * 16 + c16) * kD + pv * 128 + dt * 16 + g * 4) = acc[dt][ht];
+        for (int ht = 0; ht < 4; ++ht) ws_o[partial_block(pv, dt, ht) * kWave + lane] = acc[dt][ht];
     }
   }
   if constexpr (SPLIT) {
     // reference (of the final pass) and sum per head
     if (tid < kH) {
-      float* ws_ml = static_cast<float*>(a.ws) + int64_t(a.B) * a.S * nsplit * kH * kD;
+      float* ws_ml = partial_ml(a, nsplit);
       const int64_t slot = (qi * nsplit + split) * kH + tid;
       ws_ml[2 * slot] = mref[tid];
       ws_ml[2 * slot + 1] = lsum[0][tid] + lsum[1][tid];
@@ -433,82 +452,108 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
   }
 }
 
-// Merge the splits of one (query, head) with the sink; inverse RoPE; store.
-// grid (B*S, H/4), 256 threads: one wave per head, lane owns 8 dims; the
-// split factors are formed once per head and every split's partial is
-// fetched with several loads in flight.
+// Merge the splits of one query with the sink, inverse RoPE, store.  grid
+// (B*S, 64): workgroup y = (v, dp, ht) takes partial blocks (v, 2dp, ht) and
+// (v, 2dp + 1, ht) of every split; 256 threads, wave w sums the splits w,
+// w+4, ... (all its loads in flight at once), the four sums meet in LDS.
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int nsplit) {
-  __shared__ float rope_cs[kD];
-  __shared__ float fac[4][kMaxSplits];
+  __shared__ __attribute__((aligned(16))) float part[4][kWave][8];
+  __shared__ float sm[kMaxSplits][16], sl[kMaxSplits][16];  // (reference, sum) of the block's 16 heads
   const int64_t qi = blockIdx.x;
+  const int blk = blockIdx.y;
+  const int v = blk / 16, dp = (blk / 4) % 4, ht = blk % 4;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int h = blockIdx.y * 4 + wave;
-  const int p = a.pos[qi];
-  for (int i = tid; i < a.rope_dim / 2; i += 256) {
-    float cs, sn;
-    rope_cos_sin(p, i, a.rope_dim, a.rope_base, &cs, &sn);
-    rope_cs[2 * i] = cs;
-    rope_cs[2 * i + 1] = sn;
+  const int g = lane / 16, c16 = lane % 16;
+  const int h = ht * 16 + c16;
+  const float4* ws_o = static_cast<const float4*>(a.ws) + qi * nsplit * kPartialVecs + partial_block(v, 2 * dp, ht) * kWave + lane;
+  constexpr int kNext = 4 * kWave;  // block (v, 2dp + 1, ht) follows 4 blocks later
+  // every split's (reference, sum) of the 16 heads into LDS, four loads in flight per thread
+  {
+    const float* ml = partial_ml(a, nsplit);
+    const int n = nsplit * 16;
+    for (int i0 = tid; i0 < n; i0 += 4 * 256) {
+      float2 w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = i0 + j * 256;
+        if (i < n) w[j] = *reinterpret_cast<const float2*>(ml + 2 * ((qi * nsplit + i / 16) * kH + ht * 16 + i % 16));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = i0 + j * 256;
+        if (i < n) {
+          sm[i / 16][i % 16] = w[j].x;
+          sl[i / 16][i % 16] = w[j].y;
+        }
+      }
+    }
   }
-  const float* ws_o = static_cast<const float*>(a.ws);
-  const float* ws_ml = ws_o + int64_t(a.B) * a.S * nsplit * kH * kD;
+  __syncthreads();
+  // the head's largest reference and its sum: lanes g = 0..3 of a head take
+  // the splits s = g mod 4
   const float sink2 = a.sink[h] * kLog2e;
   float mx = sink2;
-  for (int s = lane; s < nsplit; s += kWave) mx = fmaxf(mx, ws_ml[2 * ((qi * nsplit + s) * kH + h)]);
-  mx = wave_max(mx);
-  float lsum = 0.f;
-  for (int s = lane; s < nsplit; s += kWave) {
-    const int64_t slot = (qi * nsplit + s) * kH + h;
-    const float f = fast_exp2(ws_ml[2 * slot] - mx);
-    fac[wave][s] = f;
-    lsum += ws_ml[2 * slot + 1] * f;
-  }
-  const float L = wave_sum(lsum) + fast_exp2(sink2 - mx);
-  __syncthreads();
+  for (int s = g; s < nsplit; s += 4) mx = fmaxf(mx, sm[s][c16]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+  float l = 0.f;
+  for (int s = g; s < nsplit; s += 4) l += sl[s][c16] * fast_exp2(sm[s][c16] - mx);
+  l += __shfl_xor(l, 16, kWave);
+  l += __shfl_xor(l, 32, kWave);
+  const float L = l + fast_exp2(sink2 - mx);
 
-  const int d0 = lane * 8;
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   constexpr int kBatch = 8;
-  for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
+  for (int s0 = wave; s0 < nsplit; s0 += 4 * kBatch) {
     float4 u[kBatch][2];
+    float f[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      if (s0 + j < nsplit) {
-        const float4* src = reinterpret_cast<const float4*>(ws_o + ((qi * nsplit + s0 + j) * kH + h) * kD + d0);
-        u[j][0] = src[0];
-        u[j][1] = src[1];
+      const int sp = s0 + 4 * j;
+      if (sp < nsplit) {
+        f[j] = fast_exp2(sm[sp][c16] - mx);
+        u[j][0] = ws_o[int64_t(sp) * kPartialVecs];
+        u[j][1] = ws_o[int64_t(sp) * kPartialVecs + kNext];
       }
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      if (s0 + j >= nsplit) break;
-      const float f = fac[wave][s0 + j];
-      o[0] += f * u[j][0].x; o[1] += f * u[j][0].y; o[2] += f * u[j][0].z; o[3] += f * u[j][0].w;
-      o[4] += f * u[j][1].x; o[5] += f * u[j][1].y; o[6] += f * u[j][1].z; o[7] += f * u[j][1].w;
+      if (s0 + 4 * j >= nsplit) break;
+      const float fj = f[j];
+      o[0] += fj * u[j][0].x; o[1] += fj * u[j][0].y; o[2] += fj * u[j][0].z; o[3] += fj * u[j][0].w;
+      o[4] += fj * u[j][1].x; o[5] += fj * u[j][1].y; o[6] += fj * u[j][1].z; o[7] += fj * u[j][1].w;
     }
   }
+  *reinterpret_cast<float4*>(&part[wave][lane][0]) = float4{o[0], o[1], o[2], o[3]};
+  *reinterpret_cast<float4*>(&part[wave][lane][4]) = float4{o[4], o[5], o[6], o[7]};
+  __syncthreads();
+  if (wave != 0) return;
   const float inv = 1.f / L;
+  float y[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] *= inv;
+  for (int i = 0; i < 8; ++i) y[i] = ((part[0][lane][i] + part[1][lane][i]) + (part[2][lane][i] + part[3][lane][i])) * inv;
   const int rope0 = kD - a.rope_dim;
-  if (d0 >= rope0 && p >= 0) {
+  const int p = a.pos[qi];
 #pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      const int pi = (d0 + i - rope0) / 2;
-      const float cs = rope_cs[2 * pi], sn = rope_cs[2 * pi + 1];
-      const float x0 = o[i], x1 = o[i + 1];
-      o[i] = x0 * cs + x1 * sn;
-      o[i + 1] = x1 * cs - x0 * sn;
+  for (int half = 0; half < 2; ++half) {  // dims 128v + 32dp + 16 half + 4g + 0..3
+    const int d0 = v * 128 + dp * 32 + half * 16 + g * 4;
+    float* x = &y[4 * half];
+    if (d0 >= rope0 && p >= 0) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float cs, sn;
+        rope_cos_sin(p, (d0 + 2 * u - rope0) / 2, a.rope_dim, a.rope_base, &cs, &sn);
+        const float x0 = x[2 * u], x1 = x[2 * u + 1];
+        x[2 * u] = x0 * cs + x1 * sn;
+        x[2 * u + 1] = x1 * cs - x0 * sn;
+      }
     }
-  }
-  const int64_t obase = (qi * kH + h) * kD + d0;
-  if (a.out_dtype == CSA_BF16) {
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + obase) =
-        uint4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};
-  } else {
-    float4* dst = reinterpret_cast<float4*>(static_cast<float*>(a.out) + obase);
-    dst[0] = float4{o[0], o[1], o[2], o[3]};
-    dst[1] = float4{o[4], o[5], o[6], o[7]};
+    const int64_t off = (qi * kH + h) * kD + d0;
+    if (a.out_dtype == CSA_BF16) {
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + off) = uint2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(a.out) + off) = float4{x[0], x[1], x[2], x[3]};
+    }
   }
 }
 
@@ -978,7 +1023,7 @@ AttnPlan plan_attn(int B, int S, int H, int D, int window, int nsel, int dtype, 
     return p;
   }
   if (p.nsplit > 1) {
-    p.ws_bytes = size_t(nq) * p.nsplit * kH * (size_t(kD) + 2) * sizeof(float);
+    p.ws_bytes = size_t(nq) * p.nsplit * (size_t(kPartialVecs) * 16 + kH * 2 * sizeof(float));
   } else if (nq >= kPersistMinQueries && (hca || nsel <= kPMaxSel)) {
     p.persist = true;
     p.ws_bytes = size_t(nq) * sizeof(int);  // per-query recompute flags
@@ -1010,7 +1055,7 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, bool hca, hipStr
     else if (split) hipLaunchKernelGGL((attn_mfma<false, true>), grid, dim3(kThreads), 0, stream, a, plan.nsplit, plan.chunk_rows);
     else hipLaunchKernelGGL((attn_mfma<false, false>), grid, dim3(kThreads), 0, stream, a, plan.nsplit, plan.chunk_rows);
     if (plan.nsplit > 1)
-      hipLaunchKernelGGL(attn_combine, dim3(unsigned(nq), kH / 4), dim3(256), 0, stream, a, plan.nsplit);
+      hipLaunchKernelGGL(attn_combine, dim3(unsigned(nq), kPartialVecs / kWave / 2), dim3(256), 0, stream, a, plan.nsplit);
   } else {
     const dim3 grid(unsigned(nq), a.H);
     if (hca) hipLaunchKernelGGL((attn_any<true>), grid, dim3(kWave), a.D * sizeof(float), stream, a);

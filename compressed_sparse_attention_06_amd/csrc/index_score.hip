@@ -416,6 +416,233 @@ __global__ __launch_bounds__(kDW * kWave) void index_dma(IndexArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Balanced LDS-streaming kernel (decode): a persistent grid of one workgroup
+// per CU, 8 waves.  The visible rows of all queries, cut into 16-row chunks,
+// form one query-major list of C chunks; wave k of the W waves takes chunks
+// [kC/W, (k+1)C/W), so every wave streams the same number of rows whatever
+// the sequence lengths (a grid of equal row ranges per query leaves CUs idle
+// at the end when lengths differ).  A wave streams its chunks through a
+// private four-slot LDS ring as index_dma does, loads the next query's
+// operands when its range enters that query, and sends its scores out in one
+// 1 KiB store per 256 rows.  Afterwards the workgroups share the -inf fill of
+// every row past a query's last chunk.
+// ---------------------------------------------------------------------------
+constexpr int kFlatMaxQ = 1024;  // queries whose chunk counts fit in LDS
+constexpr int kFlush = 256;      // score rows per store
+
+// s_waitcnt vmcnt(n) for a run-time n in 0..15
+__device__ __forceinline__ void wait_vmem_upto15(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(1 | (7 << 4) | (15 << 8)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(2 | (7 << 4) | (15 << 8)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(3 | (7 << 4) | (15 << 8)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(4 | (7 << 4) | (15 << 8)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(5 | (7 << 4) | (15 << 8)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(6 | (7 << 4) | (15 << 8)); break;
+    case 7: __builtin_amdgcn_s_waitcnt(7 | (7 << 4) | (15 << 8)); break;
+    case 8: __builtin_amdgcn_s_waitcnt(8 | (7 << 4) | (15 << 8)); break;
+    case 9: __builtin_amdgcn_s_waitcnt(9 | (7 << 4) | (15 << 8)); break;
+    case 10: __builtin_amdgcn_s_waitcnt(10 | (7 << 4) | (15 << 8)); break;
+    case 11: __builtin_amdgcn_s_waitcnt(11 | (7 << 4) | (15 << 8)); break;
+    case 12: __builtin_amdgcn_s_waitcnt(12 | (7 << 4) | (15 << 8)); break;
+    case 13: __builtin_amdgcn_s_waitcnt(13 | (7 << 4) | (15 << 8)); break;
+    case 14: __builtin_amdgcn_s_waitcnt(14 | (7 << 4) | (15 << 8)); break;
+    default: __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (15 << 8)); break;
+  }
+}
+
+__global__ __launch_bounds__(kDW * kWave) void index_flat(IndexArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char ring[kDW][kDSlots][kDChunk * kRowB];
+  __shared__ __attribute__((aligned(16))) float sc[kDW][kFlush];
+  __shared__ int64_t cpre[kFlatMaxQ + 1];  // chunks of the queries before q
+  __shared__ int64_t dpre[kFlatMaxQ + 1];  // 4-row groups past the chunks of the queries before q
+  __shared__ int nvis_s[kFlatMaxQ];
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int g = lane / 16, r16 = lane % 16;
+  const int nq = a.B * a.S;
+  const int Ncap = a.Ncap;
+
+  // chunk and -inf-group counts of every query, scanned by wave 0
+  if (wave == 0) {
+    const int per = (nq + kWave - 1) / kWave;
+    const int qb = lane * per;
+    int64_t cs = 0, ds = 0;
+    for (int j = 0; j < per; ++j) {
+      const int q = qb + j;
+      if (q < nq) {
+        const int nv = int(visible_entries(a.pos, q, a.ratio, Ncap));
+        nvis_s[q] = nv;
+        const int ch = (nv + kDChunk - 1) / kDChunk;
+        cs += ch;
+        ds += Ncap > ch * kDChunk ? (Ncap - ch * kDChunk) / 4 : 0;
+      }
+    }
+    int64_t ci = cs, di = ds;  // inclusive scans over lanes
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int64_t cy = __shfl_up(ci, o, kWave), dy = __shfl_up(di, o, kWave);
+      if (lane >= o) { ci += cy; di += dy; }
+    }
+    int64_t cx = ci - cs, dx = di - ds;
+    for (int j = 0; j < per; ++j) {
+      const int q = qb + j;
+      if (q < nq) {
+        cpre[q] = cx;
+        dpre[q] = dx;
+        const int nv = nvis_s[q];
+        const int ch = (nv + kDChunk - 1) / kDChunk;
+        cx += ch;
+        dx += Ncap > ch * kDChunk ? (Ncap - ch * kDChunk) / 4 : 0;
+      }
+    }
+    if (lane == kWave - 1) {
+      cpre[nq] = ci;
+      dpre[nq] = di;
+    }
+  }
+  __syncthreads();
+
+  // the query whose range holds list position c (prefix[q] <= c < prefix[q+1])
+  auto find = [&](const int64_t* pre, int64_t c) -> int {
+    int lo = 0, hi = nq;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) / 2;
+      if (pre[mid] <= c) lo = mid;
+      else hi = mid;
+    }
+    return lo;
+  };
+  struct Cur {
+    int q, lc, nch, nv;  // query, its chunk, its chunk count, its visible rows
+  };
+  auto at = [&](int64_t c) -> Cur {
+    Cur u;
+    u.q = __builtin_amdgcn_readfirstlane(find(cpre, c));
+    u.lc = __builtin_amdgcn_readfirstlane(int(c - cpre[u.q]));
+    u.nch = __builtin_amdgcn_readfirstlane(int(cpre[u.q + 1] - cpre[u.q]));
+    u.nv = __builtin_amdgcn_readfirstlane(nvis_s[u.q]);
+    return u;
+  };
+  auto advance = [&](Cur& u) {
+    if (++u.lc < u.nch) return;
+    u.lc = 0;
+    do { ++u.q; } while (u.q < nq && __builtin_amdgcn_readfirstlane(int(cpre[u.q + 1] == cpre[u.q])));
+    if (u.q < nq) {
+      u.nch = __builtin_amdgcn_readfirstlane(int(cpre[u.q + 1] - cpre[u.q]));
+      u.nv = __builtin_amdgcn_readfirstlane(nvis_s[u.q]);
+    }
+  };
+
+  const int64_t C = cpre[nq];
+  const int64_t W = int64_t(gridDim.x) * kDW;
+  const int64_t k = int64_t(blockIdx.x) * kDW + wave;
+  const int64_t c0 = k * C / W;
+  const int n = int((k + 1) * C / W - c0);  // chunks of this wave
+  const uint16_t* cache0 = static_cast<const uint16_t*>(a.cache);
+  const uint32_t ring_base = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)&ring[wave][0][0]));
+  // chunk u into ring slot `slot`: 4 copies of 4 rows; rows past the causal
+  // bound repeat the last visible row (finite, masked)
+  auto issue = [&](const Cur& u, int slot) {
+    const uint16_t* cache = cache0 + int64_t(u.q / a.S) * Ncap * kDI;
+#pragma unroll
+    for (int cp = 0; cp < kDCopies; ++cp) {
+      const int rl = cp * 4 + g;
+      const int e = min(u.lc * kDChunk + rl, u.nv - 1);
+      const uint32_t voff = uint32_t(e) * kRowB + uint32_t(((r16 ^ (rl & 15)) << 4));
+      copy_to_lds(cache, voff, ring_base + uint32_t(slot * kDChunk * kRowB + cp * 4 * kRowB));
+    }
+  };
+
+  if (n > 0) {
+    Cur ci = at(c0), cc = ci;
+    for (int j = 0; j < kDSlots - 1 && j < n; ++j) {
+      issue(ci, j);
+      advance(ci);
+    }
+    bf16x8 qa[4][4];  // [head tile][K-step]: Q[mt*16 + r16][ks*32 + g*8 .. +7]
+    float wv[4][4];
+    int q_loaded = -1;
+    int koff[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) koff[ks] = r16 * kRowB + (((ks * 4 + g) ^ r16) << 4);
+    int sq = cc.q, sb = cc.lc * kDChunk, cnt = 0;  // buffered scores: rows sb .. sb+cnt-1 of query sq
+    int f1 = 0, f2 = 0;                            // stores issued in the previous two iterations
+    auto flush = [&]() {
+      if (4 * lane < cnt && sb + 4 * lane < Ncap)
+        *reinterpret_cast<float4*>(a.scores + int64_t(sq) * Ncap + sb + 4 * lane) =
+            *reinterpret_cast<const float4*>(&sc[wave][4 * lane]);
+    };
+    for (int j = 0; j < n; ++j) {
+      // chunk j's copies are done; what was issued after them may still fly:
+      // the stores of the two previous iterations and up to two later chunks
+      wait_vmem_upto15(f1 + f2 + kDCopies * ((j + 1 < n) + (j + 2 < n)));
+      if (cc.q != q_loaded) {  // first chunk of a query in this range
+        q_loaded = cc.q;
+        const uint4* qp = reinterpret_cast<const uint4*>(a.q_idx) + int64_t(q_loaded) * (kHI * kDI / 8);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) qa[mt][ks] = as_bf16x8(qp[(mt * 16 + r16) * (kDI / 8) + ks * 4 + g]);
+        const float* wq = a.w + int64_t(q_loaded) * kHI;  // w is only 4-byte aligned
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) wv[mt][i] = wq[mt * 16 + g * 4 + i];
+      }
+      const unsigned char* tb = &ring[wave][j % kDSlots][0];
+      bf16x8 kk[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kk[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(tb + koff[ks]));
+      floatx4 acc[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][0], kk[0], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+      for (int ks = 1; ks < 4; ++ks)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][ks], kk[ks], acc[mt], 0, 0, 0);
+      float p4[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        p4[mt] = relu(acc[mt][0]) * wv[mt][0] + relu(acc[mt][1]) * wv[mt][1] + relu(acc[mt][2]) * wv[mt][2] +
+                 relu(acc[mt][3]) * wv[mt][3];
+      const float part = sum_rows4((p4[0] + p4[1]) + (p4[2] + p4[3]));
+      // scores leave when the buffer is full or the chunk starts another query
+      int f0 = 0;
+      if (cnt > 0 && (cc.q != sq || cnt == kFlush)) {
+        flush();
+        f0 = 1;
+        sq = cc.q;
+        sb = cc.lc * kDChunk;
+        cnt = 0;
+      }
+      const int e = cc.lc * kDChunk + r16;
+      if (g == 0) sc[wave][cnt + r16] = e < cc.nv ? part : -INFINITY;
+      cnt += kDChunk;
+      f2 = f1;
+      f1 = f0;
+      advance(cc);
+      // the slot of chunk j is consumed (its reads returned before the MFMAs)
+      if (j + kDSlots - 1 < n) {
+        issue(ci, (j + kDSlots - 1) % kDSlots);
+        advance(ci);
+      }
+    }
+    flush();
+  }
+
+  // -inf past every query's last chunk, in float4 groups shared by all workgroups
+  const int64_t D4 = dpre[nq];
+  const int64_t u0 = int64_t(blockIdx.x) * D4 / gridDim.x, u1 = (int64_t(blockIdx.x) + 1) * D4 / gridDim.x;
+  for (int64_t u = u0 + tid; u < u1; u += kDW * kWave) {
+    const int q = find(dpre, u);
+    const int64_t e = int64_t((nvis_s[q] + kDChunk - 1) / kDChunk) * kDChunk + 4 * (u - dpre[q]);
+    *reinterpret_cast<float4*>(a.scores + int64_t(q) * Ncap + e) = float4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Vector-ALU kernel for other shapes / fp32: one thread per (query, entry).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void index_any(IndexArgs a) {
@@ -444,6 +671,20 @@ __global__ __launch_bounds__(256) void index_any(IndexArgs a) {
 
 }  // namespace
 
+// Compute units of the current device (the persistent grid size), looked up
+// once per device.
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 hipError_t launch_index_score(const IndexArgs& a, hipStream_t stream) {
   const int64_t nq = int64_t(a.B) * a.S;
   if (nq == 0 || a.Ncap == 0) return hipSuccess;
@@ -451,9 +692,13 @@ hipError_t launch_index_score(const IndexArgs& a, hipStream_t stream) {
     const int gps = (a.S + kTQ - 1) / kTQ;
     const int ngroups = a.B * gps;
     hipLaunchKernelGGL(index_tile, dim3(unsigned(ngroups)), dim3(kTThreads), 0, stream, a, gps, ngroups);
+  } else if (a.use_mfma && a.H == kHI && a.D == kDI && a.Ncap % 4 == 0 && nq <= kFlatMaxQ &&
+             nq * int64_t(a.Ncap) >= (int64_t(1) << 21)) {
+    // long caches (>= 2M rows in all): balanced persistent streaming
+    hipLaunchKernelGGL(index_flat, dim3(unsigned(cu_count())), dim3(kDW * kWave), 0, stream, a);
   } else if (a.use_mfma && a.H == kHI && a.D == kDI && a.Ncap % 4 == 0 && nq * int64_t(a.Ncap) >= (int64_t(1) << 21)) {
-    // long caches (>= 2M rows in all): rows per wave the smallest of 32 .. 512
-    // that keeps the grid within 2048 workgroups
+    // long caches of more queries than index_flat's prefix holds: rows per
+    // wave the smallest of 32 .. 512 that keeps the grid within 2048 workgroups
     const int64_t rows = nq * int64_t(a.Ncap);
     int rw = 32;
     while (rw < 512 && rows > int64_t(2048) * kDW * rw) rw *= 2;

@@ -174,6 +174,31 @@ def test_index_score_long_cache():
         assert_normwise(got[b], want[None], what=f"b={b}")
 
 
+@pytest.mark.parametrize("B,S,Ncap", [(8, 2, 131072), (550, 2, 1920)])
+def test_index_score_long_cache_batches(B, S, Ncap):
+    """Two queries per sequence over long caches: the balanced persistent
+    kernel (16 queries) and, past its query limit, the per-query LDS kernel
+    (1,100 queries); mixed visibility, sampled queries checked in full."""
+    csa = csa_mod()
+    H, D, r = 64, 128, 4
+    rng = np.random.default_rng(30 + B)
+    n_vis = rng.integers(0, Ncap + 1, size=(B, S))
+    n_vis[0, 0], n_vis[-1, -1] = Ncap, 1
+    pos = np.where(n_vis > 0, n_vis * r + 1, -1).astype(np.int32)
+    gen = torch.Generator(device="cuda").manual_seed(31 + B)
+    q = torch.randn((B, S, H, D), generator=gen, device="cuda").to(torch.bfloat16)
+    k = torch.randn((B, Ncap, D), generator=gen, device="cuda").to(torch.bfloat16)
+    w = (torch.randn((B, S, H), generator=gen, device="cuda") / math.sqrt(D) / math.sqrt(H)).contiguous()
+    scores = torch.empty((B, S, Ncap), device="cuda")
+    csa.csa_index_score(q, w, k, dev(pos), scores, ratio=r)
+    torch.cuda.synchronize()
+    for b, s in sorted({(0, 0), (0, 1), (B // 2, 1), (B - 1, 0), (B - 1, 1)}):
+        nv = oracle.visible(int(pos[b, s]), r) if pos[b, s] >= 0 else 0
+        want = oracle.index_score(q[b, s].float().cpu().numpy().astype(np.float64), w[b, s].cpu().numpy(),
+                                  k[b].float().cpu().numpy().astype(np.float64), nv)
+        assert_normwise(scores[b, s].cpu().numpy()[None], want[None], what=f"b={b} s={s}")
+
+
 # ---------------------------------------------------------------------------
 # Top-k (identical float32 scores on both sides: bit-exact sets)
 # ---------------------------------------------------------------------------
