@@ -164,16 +164,39 @@ __device__ __forceinline__ int cand_code(const AttnArgs& a, bool hca, const Cand
   return (e >= 0 && e < a.Ncap) ? int(e) : -1;
 }
 
-// Split partials.  Split (qi, split) stores its unnormalised O (64 heads x 512
-// dims, fp32) in 128 blocks of 1 KiB, block (v, dt, ht) holding, at lane l's
-// 16 bytes, dims 128v + 16dt + 4(l/16) + 0..3 of head 16ht + l%16 -- the PV
-// waves' accumulator fragments, so that both the stores and the combine's
-// loads are whole contiguous blocks.  After all partials: (reference, sum)
-// per (qi, split, head) in fp32.
-constexpr int kPartialVecs = kH * kD * 4 / 16;  // 16-byte units per split partial
-__device__ __forceinline__ int partial_block(int v, int dt, int ht) { return (v * 8 + dt) * 4 + ht; }
+// Split partials.  Split (qi, split) stores, per head h, its part of the
+// softmax numerator O_h (512 dims) and denominator l_h against the reference
+// m_h, as O_h / l_h in fp16 scaled by 2^-e_h (e_h >= 0 the smallest exponent
+// that keeps the head's largest value below 2^15): 64 blocks of 1 KiB, block
+// (v, dp, ht) holding at lane l's 16 bytes dims 128v + 32dp + 4(l/16) + 0..3
+// and the same dims + 16 of head 16ht + l%16 -- the PV waves' accumulator
+// fragments, so that both the stores and the combine's loads are whole
+// contiguous blocks.  After all partials: (m_h, l_h, e_h, 0) per (qi, split,
+// head) in fp32.  Normalising before rounding bounds every stored value by
+// the largest |V| entry, so fp16's 11-bit significand sets the error.
+constexpr int kPartialVecs = kH * kD * 2 / 16;  // 16-byte units per split partial
+__device__ __forceinline__ int partial_block(int v, int dp, int ht) { return (v * 4 + dp) * 4 + ht; }
 __device__ __forceinline__ float* partial_ml(const AttnArgs& a, int nsplit) {
   return reinterpret_cast<float*>(static_cast<char*>(a.ws) + size_t(a.B) * a.S * nsplit * kPartialVecs * 16);
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const _Float16 a = static_cast<_Float16>(lo), b = static_cast<_Float16>(hi);  // round to nearest even
+  uint16_t ua, ub;
+  __builtin_memcpy(&ua, &a, 2);
+  __builtin_memcpy(&ub, &b, 2);
+  return uint32_t(ua) | (uint32_t(ub) << 16);
+}
+__device__ __forceinline__ float f16_lo(uint32_t pair) {
+  const uint16_t u = uint16_t(pair);
+  _Float16 h;
+  __builtin_memcpy(&h, &u, 2);
+  return static_cast<float>(h);
+}
+__device__ __forceinline__ float f16_hi(uint32_t pair) {
+  const uint16_t u = uint16_t(pair >> 16);
+  _Float16 h;
+  __builtin_memcpy(&h, &u, 2);
+  return static_cast<float>(h);
 }
 
 // ---------------------------------------------------------------------------
@@ -190,6 +213,8 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
   __shared__ float mref[kH];  // reference of the current pass, per head
   __shared__ int over_flag;
   __shared__ int codes[HCA ? 1 : kMaxChunk];
+  __shared__ float amax[SPLIT ? 4 : 1][kH];  // split partials: largest |O|/l per PV wave and head
+  __shared__ float escale[SPLIT ? kH : 1];   // split partials: the head's exponent e
 
   const int64_t qi = blockIdx.x;
   const int split = blockIdx.y;
@@ -255,16 +280,44 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
   };
   const float qk_scale = a.scale * kLog2e;
 
+  // Q (64 KiB) comes in once through the load unit, into the space of tile
+  // buffers 2 and 3 (every wave copies 8 head rows; 16-byte chunk c of head
+  // h's row sits at chunk c ^ (h % 16), so that the QK waves' reads are
+  // conflict-free), while tiles 0 and 1 copy into their buffers; the QK waves
+  // take their Q^T operands from LDS, and then tiles 2 and 3 follow.
+  const uint32_t lds_q = lds_tiles + uint32_t(2 * kT * kPitch);
+  static_assert(kH * kRowBytes <= 2 * kT * kPitch, "Q fits in two tile buffers");
+  {
+    const uint16_t* q = static_cast<const uint16_t*>(a.q) + qi * kH * kD;
+#pragma unroll
+    for (int r = 0; r < kH / kWaves; ++r) {
+      const int h = wave * (kH / kWaves) + r;
+      copy_row_to_lds(q + h * kD, uint32_t(lane ^ (h % 16)) * 16u, lds_q + uint32_t(h * kRowBytes));
+    }
+  }
+  for (int t = 0; t < n_tiles && t < 2; ++t) issue(t);
+  if (n_tiles >= 2) wait_vmem<2 * kCopyRows>();  // Q has landed; tiles 0 and 1 may still be in flight
+  else if (n_tiles == 1) wait_vmem<kCopyRows>();
+  else wait_vmem<0>();
+  __syncthreads();
+  // once Q is in the QK waves' registers, buffers 2 and 3 take tiles 2 and 3
+  auto issue_rest = [&]() {
+    __syncthreads();
+    for (int t = 2; t < n_tiles && t < kBufs; ++t) issue(t);
+  };
+
   if (wave < 4) {
     // ===================== QK waves =====================
     const int hh = wave & 1, rr = wave >> 1;  // heads hh*32.., rows rr*16.. of a tile
     bf16x8 qb[2][16];  // Q^T: Q[hh*32 + ht*16 + c16][ks*32 + g*8 .. +7]
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht) {
-      const uint16_t* q = static_cast<const uint16_t*>(a.q) + (qi * kH + hh * 32 + ht * 16 + c16) * kD + g * 8;
+      const unsigned char* qrow = &tiles[2][0] + (hh * 32 + ht * 16 + c16) * kRowBytes;
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks) qb[ht][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(q + ks * 32));
+      for (int ks = 0; ks < 16; ++ks)
+        qb[ht][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + (((ks * 4 + g) ^ c16) << 4)));
     }
+    issue_rest();
     // K chunk ks*4 + g of row rr*16 + c16 sits 128 B further (K-steps with
     // bit 1 clear) or nearer (bit 1 set) when the row is flipped
     const int k_base = (rr * 16 + c16) * kPitch + g * 16;
@@ -281,7 +334,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
         l_run[ht] = (!SPLIT && rr == 0 && g == 0) ? fast_exp2(s2 - m_ref[ht]) : 0.f;
         m_run[ht] = -INFINITY;
       }
-      prologue();
+      if (pass > 0) prologue();
       for (int s = 0; s <= n_tiles; ++s) {
         step_sync(s);
         if (s == n_tiles) break;
@@ -346,9 +399,23 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
       __syncthreads();  // every wave has read the flag and the maxima
       if (tid == 0) over_flag = 0;
     }
+    if constexpr (SPLIT) {
+      __syncthreads();  // the PV waves' largest values
+      if (tid < kH) {
+        const float am = fmaxf(fmaxf(amax[0][tid], amax[1][tid]), fmaxf(amax[2][tid], amax[3][tid]));
+        // am < 2^ex; e keeps am * 2^-e below 2^15
+        const int ex = am > 0.f ? int((__float_as_uint(am) >> 23) & 0xffu) - 126 : 0;
+        const int e = ex > 15 ? ex - 15 : 0;
+        escale[tid] = float(e);
+        float4* ml = reinterpret_cast<float4*>(partial_ml(a, nsplit));
+        ml[(qi * nsplit + split) * kH + tid] = float4{mref[tid], lsum[0][tid] + lsum[1][tid], float(e), 0.f};
+      }
+      __syncthreads();  // the exponents
+    }
   } else {
     // ===================== PV waves =====================
     const int pv = wave - 4;  // dims pv*128 .. +128
+    issue_rest();
     // V^T operand: rows g*8 + h*4 + c16/4 (h = half of the 8-row K-slice),
     // dims pv*128 + dt*16 + 4*(c16 % 4) .. +3; a flipped row (bit 2 = h,
     // bit 3 = g & 1) holds the chunk 128 B further (dt < 4) or nearer (dt >= 4)
@@ -362,7 +429,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
       for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) acc[dt][ht] = floatx4{0.f, 0.f, 0.f, 0.f};
-      prologue();
+      if (pass > 0) prologue();
       for (int s = 0; s <= n_tiles; ++s) {
         step_sync(s);
         if (s == 0) continue;
@@ -432,51 +499,71 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
         }
       }
     } else {
-      // unnormalised partial O in fragment order: every store is one
-      // contiguous 1 KiB block (see partial_block)
-      floatx4* ws_o = static_cast<floatx4*>(a.ws) + (qi * nsplit + split) * kPartialVecs;
+      // O / l per head, its largest magnitude over this wave's dims to LDS
+      float inv[4];
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
+      for (int ht = 0; ht < 4; ++ht) {
+        inv[ht] = L[ht] > 0.f ? 1.f / L[ht] : 0.f;
+        float m = 0.f;
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht) ws_o[partial_block(pv, dt, ht) * kWave + lane] = acc[dt][ht];
-    }
-  }
-  if constexpr (SPLIT) {
-    // reference (of the final pass) and sum per head
-    if (tid < kH) {
-      float* ws_ml = partial_ml(a, nsplit);
-      const int64_t slot = (qi * nsplit + split) * kH + tid;
-      ws_ml[2 * slot] = mref[tid];
-      ws_ml[2 * slot + 1] = lsum[0][tid] + lsum[1][tid];
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(acc[dt][ht][i]));
+        m = max_rows4(m);
+        if (g == 0) amax[pv][ht * 16 + c16] = m * inv[ht];
+      }
+      __syncthreads();  // largest values in
+      __syncthreads();  // exponents out
+      uint4* ws_o = static_cast<uint4*>(a.ws) + (qi * nsplit + split) * kPartialVecs;
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) {
+        const float f = inv[ht] * __uint_as_float(uint32_t(127 - int(escale[ht * 16 + c16])) << 23);  // inv * 2^-e
+#pragma unroll
+        for (int dp = 0; dp < 4; ++dp) {
+          const floatx4 x = acc[2 * dp][ht], y = acc[2 * dp + 1][ht];
+          ws_o[partial_block(pv, dp, ht) * kWave + lane] =
+              uint4{pack_f16x2(x[0] * f, x[1] * f), pack_f16x2(x[2] * f, x[3] * f), pack_f16x2(y[0] * f, y[1] * f),
+                    pack_f16x2(y[2] * f, y[3] * f)};
+        }
+      }
     }
   }
 }
 
 // Merge the splits of one query with the sink, inverse RoPE, store.  grid
-// (B*S, 64): workgroup y = (v, dp, ht) takes partial blocks (v, 2dp, ht) and
-// (v, 2dp + 1, ht) of every split; 256 threads, wave w sums the splits w,
-// w+4, ... (all its loads in flight at once), the four sums meet in LDS.
+// (B*S, 64): workgroup y = (v, dp, ht) takes partial block y of every split;
+// 256 threads, wave w sums the splits w, w+4, ... (all its loads in flight
+// at once), the four sums meet in LDS.
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int nsplit) {
   __shared__ __attribute__((aligned(16))) float part[4][kWave][8];
-  __shared__ float sm[kMaxSplits][16], sl[kMaxSplits][16];  // (reference, sum) of the block's 16 heads
+  // per split and head of the block: reference, sum, log2 of the stored scale
+  __shared__ float sm[kMaxSplits][16], sl[kMaxSplits][16], se[kMaxSplits][16];
   const int64_t qi = blockIdx.x;
   const int blk = blockIdx.y;
   const int v = blk / 16, dp = (blk / 4) % 4, ht = blk % 4;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int g = lane / 16, c16 = lane % 16;
   const int h = ht * 16 + c16;
-  const float4* ws_o = static_cast<const float4*>(a.ws) + qi * nsplit * kPartialVecs + partial_block(v, 2 * dp, ht) * kWave + lane;
-  constexpr int kNext = 4 * kWave;  // block (v, 2dp + 1, ht) follows 4 blocks later
-  // every split's (reference, sum) of the 16 heads into LDS, four loads in flight per thread
+  const uint4* ws_o = static_cast<const uint4*>(a.ws) + qi * nsplit * kPartialVecs + blk * kWave + lane;
+  // this wave's partials (splits wave, wave + 4, ...) are requested first:
+  // they need no record, so their latency overlaps the records' own
+  constexpr int kBatch = kMaxSplits / 4 / 4;  // splits per wave held at once
+  uint4 u[kBatch];
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) {
+    const int sp = wave + 4 * j;
+    if (sp < nsplit) u[j] = ws_o[int64_t(sp) * kPartialVecs];
+  }
+  // every split's record for the 16 heads into LDS, four loads in flight per thread
   {
-    const float* ml = partial_ml(a, nsplit);
+    const float4* ml = reinterpret_cast<const float4*>(partial_ml(a, nsplit));
     const int n = nsplit * 16;
     for (int i0 = tid; i0 < n; i0 += 4 * 256) {
-      float2 w[4];
+      float4 w[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i = i0 + j * 256;
-        if (i < n) w[j] = *reinterpret_cast<const float2*>(ml + 2 * ((qi * nsplit + i / 16) * kH + ht * 16 + i % 16));
+        if (i < n) w[j] = ml[(qi * nsplit + i / 16) * kH + ht * 16 + i % 16];
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -484,6 +571,7 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int nsplit) {
         if (i < n) {
           sm[i / 16][i % 16] = w[j].x;
           sl[i / 16][i % 16] = w[j].y;
+          se[i / 16][i % 16] = w[j].z;
         }
       }
     }
@@ -494,34 +582,28 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int nsplit) {
   const float sink2 = a.sink[h] * kLog2e;
   float mx = sink2;
   for (int s = g; s < nsplit; s += 4) mx = fmaxf(mx, sm[s][c16]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+  mx = max_rows4(mx);
   float l = 0.f;
   for (int s = g; s < nsplit; s += 4) l += sl[s][c16] * fast_exp2(sm[s][c16] - mx);
-  l += __shfl_xor(l, 16, kWave);
-  l += __shfl_xor(l, 32, kWave);
-  const float L = l + fast_exp2(sink2 - mx);
+  const float L = sum_rows4(l) + fast_exp2(sink2 - mx);
 
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  constexpr int kBatch = 8;
   for (int s0 = wave; s0 < nsplit; s0 += 4 * kBatch) {
-    float4 u[kBatch][2];
-    float f[kBatch];
+    if (s0 != wave) {  // more than kBatch splits per wave
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int sp = s0 + 4 * j;
-      if (sp < nsplit) {
-        f[j] = fast_exp2(sm[sp][c16] - mx);
-        u[j][0] = ws_o[int64_t(sp) * kPartialVecs];
-        u[j][1] = ws_o[int64_t(sp) * kPartialVecs + kNext];
+      for (int j = 0; j < kBatch; ++j) {
+        const int sp = s0 + 4 * j;
+        if (sp < nsplit) u[j] = ws_o[int64_t(sp) * kPartialVecs];
       }
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      if (s0 + 4 * j >= nsplit) break;
-      const float fj = f[j];
-      o[0] += fj * u[j][0].x; o[1] += fj * u[j][0].y; o[2] += fj * u[j][0].z; o[3] += fj * u[j][0].w;
-      o[4] += fj * u[j][1].x; o[5] += fj * u[j][1].y; o[6] += fj * u[j][1].z; o[7] += fj * u[j][1].w;
+      const int sp = s0 + 4 * j;
+      if (sp < nsplit) {
+        const float fj = sl[sp][c16] * fast_exp2(sm[sp][c16] + se[sp][c16] - mx);  // l_s 2^(m_s - mx + e_s)
+        o[0] += fj * f16_lo(u[j].x); o[1] += fj * f16_hi(u[j].x); o[2] += fj * f16_lo(u[j].y); o[3] += fj * f16_hi(u[j].y);
+        o[4] += fj * f16_lo(u[j].z); o[5] += fj * f16_hi(u[j].z); o[6] += fj * f16_lo(u[j].w); o[7] += fj * f16_hi(u[j].w);
+      }
     }
   }
   *reinterpret_cast<float4*>(&part[wave][lane][0]) = float4{o[0], o[1], o[2], o[3]};
@@ -1023,7 +1105,7 @@ AttnPlan plan_attn(int B, int S, int H, int D, int window, int nsel, int dtype, 
     return p;
   }
   if (p.nsplit > 1) {
-    p.ws_bytes = size_t(nq) * p.nsplit * (size_t(kPartialVecs) * 16 + kH * 2 * sizeof(float));
+    p.ws_bytes = size_t(nq) * p.nsplit * (size_t(kPartialVecs) * 16 + kH * 4 * sizeof(float));
   } else if (nq >= kPersistMinQueries && (hca || nsel <= kPMaxSel)) {
     p.persist = true;
     p.ws_bytes = size_t(nq) * sizeof(int);  // per-query recompute flags
@@ -1055,7 +1137,7 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, bool hca, hipStr
     else if (split) hipLaunchKernelGGL((attn_mfma<false, true>), grid, dim3(kThreads), 0, stream, a, plan.nsplit, plan.chunk_rows);
     else hipLaunchKernelGGL((attn_mfma<false, false>), grid, dim3(kThreads), 0, stream, a, plan.nsplit, plan.chunk_rows);
     if (plan.nsplit > 1)
-      hipLaunchKernelGGL(attn_combine, dim3(unsigned(nq), kPartialVecs / kWave / 2), dim3(256), 0, stream, a, plan.nsplit);
+      hipLaunchKernelGGL(attn_combine, dim3(unsigned(nq), kPartialVecs / kWave), dim3(256), 0, stream, a, plan.nsplit);
   } else {
     const dim3 grid(unsigned(nq), a.H);
     if (hca) hipLaunchKernelGGL((attn_any<true>), grid, dim3(kWave), a.D * sizeof(float), stream, a);

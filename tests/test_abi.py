@@ -124,7 +124,7 @@ def test_sparse_attn_rejects(lib, bad):
 
 def test_attn_workspace_sizes(lib):
     ws = lib.csa_sparse_attn_workspace_size(8, 1, 64, 512, 512, 128)
-    assert ws > 0 and ws % (8 * 64 * (512 + 2) * 4) == 0  # whole (query, split) partials: O, (m, l) in fp32
+    assert ws > 0 and ws % (8 * 64 * (512 * 2 + 16)) == 0  # whole (query, split) partials: fp16 O/l, fp32 records
     # many queries: one persistent pass, one recompute flag per query
     assert lib.csa_sparse_attn_workspace_size(1, 8192, 64, 512, 512, 128) == 8192 * 4
     assert lib.csa_sparse_attn_workspace_size(1, 300, 64, 512, 512, 128) == 0  # one split per query
