@@ -378,10 +378,8 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
       // ---- per-head sums and maxima of this wave's rows
 #pragma unroll
       for (int ht = 0; ht < 2; ++ht) {
-        float l = l_run[ht] + __shfl_xor(l_run[ht], 16, kWave);
-        l += __shfl_xor(l, 32, kWave);
-        float m = fmaxf(m_run[ht], __shfl_xor(m_run[ht], 16, kWave));
-        m = fmaxf(m, __shfl_xor(m, 32, kWave));
+        const float l = sum_rows4(l_run[ht]);
+        const float m = max_rows4(m_run[ht]);
         if (g == 0) {
           lsum[rr][hh * 32 + ht * 16 + c16] = l;
           mseen[rr][hh * 32 + ht * 16 + c16] = m;

@@ -52,17 +52,58 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
 }
 
 // ---------------------------------------------------------------------------
-// Wave reductions (64 lanes)
+// Wave reductions and scans (64 lanes), register to register.  Within each
+// 16-lane row, DPP lane moves: the two quad swaps (lane ^ 1, lane ^ 2), then
+// the half-row mirror (lane 7 - i: the other quad of the half row) and the
+// row mirror (lane 15 - i: the other half row), after which every lane of a
+// row holds the row's result; the four rows then meet through the permlane
+// swaps (lanes l ^ 32, then l ^ 16).
 // ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t x) {
+  return uint32_t(__builtin_amdgcn_mov_dpp(int(x), CTRL, 0xF, 0xF, false));
+}
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_bits(uint32_t x, Op op) {
+  x = op(x, dpp_move<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = op(x, dpp_move<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = op(x, dpp_move<0x141>(x));  // row_half_mirror
+  x = op(x, dpp_move<0x140>(x));  // row_mirror
+  const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  x = op(p[0], p[1]);
+  const auto q = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return op(q[0], q[1]);
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return __uint_as_float(wave_reduce_bits(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  return __uint_as_float(wave_reduce_bits(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
+}
+__device__ __forceinline__ float wave_min(float v) {
+  return __uint_as_float(wave_reduce_bits(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fminf(__uint_as_float(a), __uint_as_float(b)));
+  }));
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  return wave_reduce_bits(v, [](uint32_t a, uint32_t b) { return a + b; });
+}
+// Inclusive prefix sum over the wave's lanes: row_shr 1, 2, 4, 8 within each
+// row (lanes shifted in from outside the row add 0), then every row adds the
+// totals of the rows below it (lanes 15, 31, 47).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x111, 0xF, 0xF, false));
+  x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x112, 0xF, 0xF, false));
+  x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x114, 0xF, 0xF, false));
+  x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x118, 0xF, 0xF, false));
+  const uint32_t r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+                 r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = int(threadIdx.x % kWave) >> 4;
+  return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
 }
 
 // ---------------------------------------------------------------------------

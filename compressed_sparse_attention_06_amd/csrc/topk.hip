@@ -42,29 +42,12 @@ __device__ __forceinline__ float key_value(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
-__device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-
 // Exclusive scan over the block; returns the exclusive prefix, *total the sum.
 template <int THREADS>
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
   constexpr int W = THREADS / kWave;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_scan(v);
   if (lane == kWave - 1) wsum[wave] = x;
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -91,6 +74,13 @@ struct SelectArgs {
   uint32_t* okey;         // chunked: [R, nchunks*k]
   int* oidx;
 };
+
+// LDS position of staged key i: 16-byte chunk i/4 moves to chunk
+// (i/4) ^ ((i/64) % 16).  A thread's run of 16 keys (four chunks 64 bytes
+// apart from its neighbours') then spreads over all bank groups when read as
+// 16-byte vectors, and the coalesced writes of 64 consecutive keys stay a
+// permutation of 16 consecutive chunks.
+__device__ __forceinline__ int lds_swizzle(int i) { return (((i >> 2) ^ ((i >> 6) & 15)) << 2) | (i & 3); }
 
 template <int THREADS, int ITEMS, bool FROM_CAND, bool FINAL>
 __global__ __launch_bounds__(THREADS) void topk_select(SelectArgs a) {
@@ -149,8 +139,8 @@ __global__ __launch_bounds__(THREADS) void topk_select(SelectArgs a) {
     }
 #pragma unroll
     for (int t = 0; t < ITEMS; ++t) {
-      keys[tid + t * THREADS] = kin[t];
-      if constexpr (FROM_CAND) idxs[tid + t * THREADS] = iin[t];
+      keys[lds_swizzle(tid + t * THREADS)] = kin[t];
+      if constexpr (FROM_CAND) idxs[lds_swizzle(tid + t * THREADS)] = iin[t];
     }
   }
   __syncthreads();
@@ -158,10 +148,10 @@ __global__ __launch_bounds__(THREADS) void topk_select(SelectArgs a) {
   int kidx[FROM_CAND ? ITEMS : 1];
 #pragma unroll
   for (int t = 0; t < ITEMS; t += 4) {
-    const uint4 v = *reinterpret_cast<const uint4*>(&keys[tid * ITEMS + t]);
+    const uint4 v = *reinterpret_cast<const uint4*>(&keys[lds_swizzle(tid * ITEMS + t)]);
     key[t] = v.x; key[t + 1] = v.y; key[t + 2] = v.z; key[t + 3] = v.w;
     if constexpr (FROM_CAND) {
-      const int4 w = *reinterpret_cast<const int4*>(&idxs[tid * ITEMS + t]);
+      const int4 w = *reinterpret_cast<const int4*>(&idxs[lds_swizzle(tid * ITEMS + t)]);
       kidx[t] = w.x; kidx[t + 1] = w.y; kidx[t + 2] = w.z; kidx[t + 3] = w.w;
     }
   }
@@ -210,12 +200,7 @@ __global__ __launch_bounds__(THREADS) void topk_select(SelectArgs a) {
         for (int w = 0; w < W; ++w) cnt[j] += hist[w][255 - 4 * lane - j];
         own += cnt[j];
       }
-      uint32_t incl = own;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t y = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += y;
-      }
+      const uint32_t incl = wave_incl_scan(own);
       uint32_t above = incl - own;  // keys in bins above this lane's
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -226,11 +211,17 @@ __global__ __launch_bounds__(THREADS) void topk_select(SelectArgs a) {
     __syncthreads();
     const uint32_t sel_bin = sh_bin;
     uint32_t remaining = a.k - sh_above;  // how many keys of that bin are kept
+    // one LDS atomic per wave and item slot: lanes take consecutive places
 #pragma unroll
     for (int t = 0; t < ITEMS; ++t) {
-      if (key[t] != 0u && bin(key[t]) == sel_bin) {
-        const uint32_t at = atomicAdd(&nlist, 1u);
-        if (at < THREADS) list[at] = key[t];
+      const bool m = key[t] != 0u && bin(key[t]) == sel_bin;
+      const uint64_t bal = __ballot(m);
+      if (bal != 0) {
+        uint32_t at0 = 0;
+        if (lane == 0) at0 = atomicAdd(&nlist, uint32_t(__popcll(bal)));
+        at0 = __builtin_amdgcn_readfirstlane(at0);
+        const uint32_t at = at0 + uint32_t(__builtin_amdgcn_mbcnt_hi(uint32_t(bal >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(bal), 0)));
+        if (m && at < THREADS) list[at] = key[t];
       }
     }
     __syncthreads();
