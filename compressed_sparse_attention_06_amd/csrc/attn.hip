@@ -535,7 +535,11 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int nsplit) {
   __shared__ __attribute__((aligned(16))) float part[4][kWave][8];
   // per split and head of the block: reference, sum, log2 of the stored scale
-  __shared__ float sm[kMaxSplits][16], sl[kMaxSplits][16], se[kMaxSplits][16];
+  // (3 x nsplit x 16 floats of dynamic LDS)
+  extern __shared__ float rec[];
+  float (*sm)[16] = reinterpret_cast<float (*)[16]>(rec);
+  float (*sl)[16] = reinterpret_cast<float (*)[16]>(rec + nsplit * 16);
+  float (*se)[16] = reinterpret_cast<float (*)[16]>(rec + 2 * nsplit * 16);
   const int64_t qi = blockIdx.x;
   const int blk = blockIdx.y;
   const int v = blk / 16, dp = (blk / 4) % 4, ht = blk % 4;
@@ -1135,7 +1139,8 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, bool hca, hipStr
     else if (split) hipLaunchKernelGGL((attn_mfma<false, true>), grid, dim3(kThreads), 0, stream, a, plan.nsplit, plan.chunk_rows);
     else hipLaunchKernelGGL((attn_mfma<false, false>), grid, dim3(kThreads), 0, stream, a, plan.nsplit, plan.chunk_rows);
     if (plan.nsplit > 1)
-      hipLaunchKernelGGL(attn_combine, dim3(unsigned(nq), kPartialVecs / kWave), dim3(256), 0, stream, a, plan.nsplit);
+      hipLaunchKernelGGL(attn_combine, dim3(unsigned(nq), kPartialVecs / kWave), dim3(256),
+                         size_t(3) * plan.nsplit * 16 * sizeof(float), stream, a, plan.nsplit);
   } else {
     const dim3 grid(unsigned(nq), a.H);
     if (hca) hipLaunchKernelGGL((attn_any<true>), grid, dim3(kWave), a.D * sizeof(float), stream, a);
