@@ -153,6 +153,11 @@ class DecodeWorkload:
             import compressed_sparse_attention_06_amd as csa
             self.ws_attn = torch.empty(max(1, csa.hca_attn_workspace_size(B, 1, cfg.H, D, self.Ncap, cfg.window)),
                                        dtype=torch.uint8, device=device)
+        # compressor workspaces: zero-filled once, one per role (the roles may run concurrently)
+        self.ws_ckv = torch.zeros(max(16, csa.csa_compress_workspace_size(B, D, cfg.ratio, cfg.overlap)),
+                                  dtype=torch.uint8, device=device)
+        self.ws_cidx = torch.zeros(max(16, csa.csa_compress_workspace_size(B, cfg.D_I, cfg.ratio, cfg.overlap)),
+                                   dtype=torch.uint8, device=device)
         torch.cuda.synchronize()
 
     @property
@@ -169,13 +174,13 @@ class DecodeWorkload:
         scale = 1.0 / math.sqrt(cfg.D)
         L = [("compress_kv", lambda: csa.csa_compress(
             self.kv_stage, self.gate_stage, self.gamma, self.kv[c], ratio=cfg.ratio, overlap=cfg.overlap,
-            rope_dim=cfg.rope_dim, rope_base=cfg.rope_base, eps=cfg.eps, pos=self.pos))]
+            rope_dim=cfg.rope_dim, rope_base=cfg.rope_base, eps=cfg.eps, pos=self.pos, ws=self.ws_ckv))]
         if cfg.csa:
             L += [
                 ("compress_idx", lambda: csa.csa_compress(
                     self.ki_stage, self.gi_stage, self.gamma_idx, self.idx_cache[c], ratio=cfg.ratio,
                     overlap=cfg.overlap, rope_dim=cfg.rope_dim_idx, rope_base=cfg.rope_base, eps=cfg.eps,
-                    pos=self.pos)),
+                    pos=self.pos, ws=self.ws_cidx)),
                 ("index_score", lambda: csa.csa_index_score(self.q_idx, self.w, self.idx_cache[c], self.pos2,
                                                             self.scores, ratio=cfg.ratio)),
                 ("topk", lambda: csa.csa_topk(self.scores.view(cfg.B, self.Ncap), None, cfg.k,
@@ -268,7 +273,15 @@ class PrefillWorkload:
                                    device=device)
         self.ws_attn = torch.empty(max(1, csa.csa_sparse_attn_workspace_size(1, S, cfg.H, D, cfg.k, cfg.window)),
                                    dtype=torch.uint8, device=device)
+        self.ws_ckv = torch.zeros(max(16, csa.csa_compress_workspace_size(self.Nc, D, cfg.ratio, cfg.overlap)),
+                                  dtype=torch.uint8, device=device)
+        self.ws_cidx = torch.zeros(max(16, csa.csa_compress_workspace_size(self.Nc, DI, cfg.ratio, cfg.overlap)),
+                                   dtype=torch.uint8, device=device)
         torch.cuda.synchronize()
+
+    # the KV-role compressor feeds only the attention: it runs beside the index chain
+    side_kernels = ("compress_kv",)
+    join_before = "sparse_attn"
 
     def launches(self, c):
         import compressed_sparse_attention_06_amd as csa
@@ -276,10 +289,11 @@ class PrefillWorkload:
         c = c % self.copies
         return [
             ("compress_kv", lambda: csa.csa_compress(self.kv, self.gate, self.gamma, self.kv_cache, ratio=cfg.ratio,
-                                                     overlap=cfg.overlap, rope_dim=cfg.rope_dim, eps=cfg.eps)),
+                                                     overlap=cfg.overlap, rope_dim=cfg.rope_dim, eps=cfg.eps,
+                                                     ws=self.ws_ckv)),
             ("compress_idx", lambda: csa.csa_compress(self.ki, self.gi, self.gamma_idx, self.idx_cache,
                                                       ratio=cfg.ratio, overlap=cfg.overlap,
-                                                      rope_dim=cfg.rope_dim_idx, eps=cfg.eps)),
+                                                      rope_dim=cfg.rope_dim_idx, eps=cfg.eps, ws=self.ws_cidx)),
             ("index_score", lambda: csa.csa_index_score(self.q_idx[c], self.w, self.idx_cache, self.pos,
                                                         self.scores, ratio=cfg.ratio)),
             ("topk", lambda: csa.csa_topk(self.scores.view(S, self.Nc), None, cfg.k, self.sel.view(S, cfg.k),

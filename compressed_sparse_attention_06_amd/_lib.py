@@ -25,8 +25,10 @@ _c_int, _c_i64, _c_f, _c_sz, _c_p = ctypes.c_int, ctypes.c_int64, ctypes.c_float
 SIGNATURES = {
     "csa_status_string": (ctypes.c_char_p, [_c_int]),
     "csa_version": (_c_int, []),
+    "csa_compress_workspace_size": (_c_sz, [_c_i64, _c_int, _c_int, _c_int]),
     "csa_compress": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_int, _c_p, _c_int, _c_int, _c_i64, _c_int, _c_int, _c_int,
-                              _c_int, _c_f, _c_f, _c_int, _c_int, _c_int, _c_p, _c_p, _c_int, _c_i64, _c_int, _c_p]),
+                              _c_int, _c_f, _c_f, _c_int, _c_int, _c_int, _c_p, _c_p, _c_int, _c_i64, _c_int, _c_p,
+                              _c_sz, _c_p]),
     "csa_index_score": (_c_int, [_c_p, _c_p, _c_p, _c_int, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                  _c_p, _c_p]),
     "csa_topk_workspace_size": (_c_sz, [_c_int, _c_int, _c_int]),
@@ -108,11 +110,21 @@ def _rows(t):
 
 
 # ---------------------------------------------------------------------------
+def csa_compress_workspace_size(entries, D, ratio, overlap):
+    return int(lib().csa_compress_workspace_size(entries, D, ratio, overlap))
+
+
 def csa_compress(kv, gate, gamma, out, *, ratio, overlap, rope_dim, rope_base=10000.0, eps=1e-6,
-                 kv_prev=None, gate_prev=None, tok0=0, e0=0, n_entries=None, pos=None, stream=None):
-    """kv, gate: [B, T, D] (rows contiguous); out: [B, out_cap, D]; pos: [B] int32 (ring mode) or None."""
+                 kv_prev=None, gate_prev=None, tok0=0, e0=0, n_entries=None, pos=None, ws=None, stream=None):
+    """kv, gate: [B, T, D] (rows contiguous); out: [B, out_cap, D]; pos: [B] int32 (ring mode) or None.
+
+    ws: a zero-filled uint8 device tensor of at least csa_compress_workspace_size bytes (kept by the
+    caller across calls, each of which leaves it ready for the next), or None to allocate one."""
     B, T, D = kv.shape
     n = (out.shape[1] - e0) if n_entries is None else n_entries
+    need = csa_compress_workspace_size(B if pos is not None else B * n, D, ratio, overlap)
+    if need and (ws is None or _bytes(ws) < need):
+        ws = torch.zeros(need, dtype=torch.uint8, device=kv.device)
     bstride = _rows(kv)
     for t in (gate, kv_prev, gate_prev):
         if t is not None and (t.shape != kv.shape or _rows(t) != bstride):
@@ -120,7 +132,8 @@ def csa_compress(kv, gate, gamma, out, *, ratio, overlap, rope_dim, rope_base=10
     _dense(gamma, pos)
     st = lib().csa_compress(_ptr(kv), _ptr(gate), _ptr(kv_prev), _ptr(gate_prev), _dtype(kv), _ptr(gamma), B, T,
                             bstride, D, ratio, overlap, rope_dim, rope_base, eps, tok0, e0, n, _ptr(pos),
-                            _ptr(out), _dtype(out), _rows(out), out.shape[1], _stream(stream))
+                            _ptr(out), _dtype(out), _rows(out), out.shape[1], _ptr(ws), _bytes(ws),
+                            _stream(stream))
     _check(st, "csa_compress")
     return out
 

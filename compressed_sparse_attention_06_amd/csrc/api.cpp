@@ -34,10 +34,16 @@ const char* csa_status_string(int status) {
 
 int csa_version(void) { return kVersion; }
 
+size_t csa_compress_workspace_size(int64_t entries, int D, int ratio, int overlap) {
+  if (entries < 0 || D < 1 || D > 8192 || ratio < 1 || (overlap != 0 && overlap != 1)) return 0;
+  return csa::plan_compress(entries, D, ratio, overlap).ws_bytes;
+}
+
 int csa_compress(const void* kv, const void* gate, const void* kv_prev, const void* gate_prev, int in_dtype,
                  const float* gamma, int B, int T, int64_t in_bstride, int D, int ratio, int overlap,
                  int rope_dim, float rope_base, float eps, int tok0, int e0, int n_entries, const int* pos,
-                 void* out, int out_dtype, int64_t out_bstride, int out_cap, hipStream_t stream) {
+                 void* out, int out_dtype, int64_t out_bstride, int out_cap, void* ws, size_t ws_bytes,
+                 hipStream_t stream) {
   if (!kv || !gate || !gamma || !out) return CSA_ERR_INVALID_ARG;
   if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return CSA_ERR_INVALID_ARG;
   if (B < 0 || T < 1 || D < 1 || ratio < 1 || (overlap != 0 && overlap != 1)) return CSA_ERR_INVALID_ARG;
@@ -56,6 +62,11 @@ int csa_compress(const void* kv, const void* gate, const void* kv_prev, const vo
   } else {
     if (int64_t(T) < int64_t(1 + overlap) * ratio) return CSA_ERR_INVALID_ARG;
   }
+  const int64_t entries = pos == nullptr ? int64_t(B) * n_entries : B;
+  if (entries > INT32_MAX) return CSA_ERR_UNSUPPORTED;
+  const csa::CompressPlan plan = csa::plan_compress(entries, D, ratio, overlap);
+  if (plan.ws_bytes > 0 && (ws == nullptr || ws_bytes < plan.ws_bytes)) return CSA_ERR_WORKSPACE;
+  if (plan.ws_bytes > 0 && !aligned16(ws)) return CSA_ERR_INVALID_ARG;
   csa::CompressArgs a{};
   a.kv = kv;
   a.gate = gate;
@@ -71,6 +82,7 @@ int csa_compress(const void* kv, const void* gate, const void* kv_prev, const vo
   a.overlap = overlap;
   a.rope_dim = rope_dim;
   a.rope_base = rope_base;
+  a.rope_log2_base = std::log2(double(rope_base));
   a.eps = eps;
   a.tok0 = tok0;
   a.e0 = e0;
@@ -80,7 +92,8 @@ int csa_compress(const void* kv, const void* gate, const void* kv_prev, const vo
   a.out_dtype = out_dtype;
   a.out_bstride = out_bstride;
   a.out_cap = out_cap;
-  return hip_status(csa::launch_compress(a, stream));
+  a.ws = ws;
+  return hip_status(csa::launch_compress(a, plan, stream));
 }
 
 int csa_index_score(const void* q_idx, const float* w, const void* idx_cache, int dtype, const int* pos, int B,
@@ -163,6 +176,7 @@ int attn_common(const void* q, const void* cmp, int Ncap, const int* idx, int k,
   a.scale = scale;
   a.rope_dim = rope_dim;
   a.rope_base = rope_base;
+  a.rope_log2_base = std::log2(double(rope_base));
   a.B = B;
   a.S = S;
   a.H = H;

@@ -471,7 +471,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
         const bool rot = d0 >= rope0 && c.p >= 0;
         if (rot) {
 #pragma unroll
-          for (int u = 0; u < 2; ++u) rope_cos_sin(c.p, (d0 + 2 * u - rope0) / 2, a.rope_dim, a.rope_base, &cs[u], &sn[u]);
+          for (int u = 0; u < 2; ++u) rope_cos_sin(c.p, (d0 + 2 * u - rope0) / 2, a.rope_dim, a.rope_log2_base, &cs[u], &sn[u]);
         }
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) {
@@ -626,7 +626,7 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int nsplit) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         float cs, sn;
-        rope_cos_sin(p, (d0 + 2 * u - rope0) / 2, a.rope_dim, a.rope_base, &cs, &sn);
+        rope_cos_sin(p, (d0 + 2 * u - rope0) / 2, a.rope_dim, a.rope_log2_base, &cs, &sn);
         const float x0 = x[2 * u], x1 = x[2 * u + 1];
         x[2 * u] = x0 * cs + x1 * sn;
         x[2 * u + 1] = x1 * cs - x0 * sn;
@@ -960,7 +960,7 @@ __global__ __launch_bounds__(kThreads) void attn_persist(AttnArgs a, int* redo) 
           const bool rot = d0 >= rope0 && p >= 0;
           if (rot) {
 #pragma unroll
-            for (int u = 0; u < 2; ++u) rope_cos_sin(p, (d0 + 2 * u - rope0) / 2, a.rope_dim, a.rope_base, &cs[u], &sn[u]);
+            for (int u = 0; u < 2; ++u) rope_cos_sin(p, (d0 + 2 * u - rope0) / 2, a.rope_dim, a.rope_log2_base, &cs[u], &sn[u]);
           }
 #pragma unroll
           for (int ht = 0; ht < 4; ++ht) {
@@ -1047,7 +1047,7 @@ __device__ __forceinline__ void attn_head(const AttnArgs a, int64_t qi, int h, f
   if (c.p >= 0) {
     for (int i = lane; i < a.rope_dim / 2; i += kWave) {
       float cs, sn;
-      rope_cos_sin(c.p, i, a.rope_dim, a.rope_base, &cs, &sn);
+      rope_cos_sin(c.p, i, a.rope_dim, a.rope_log2_base, &cs, &sn);
       const float x0 = obuf[rope0 + 2 * i], x1 = obuf[rope0 + 2 * i + 1];
       obuf[rope0 + 2 * i] = x0 * cs + x1 * sn;
       obuf[rope0 + 2 * i + 1] = x1 * cs - x0 * sn;

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "csa.h"
+#include "rope_math.h"
 
 namespace csa {
 
@@ -107,23 +108,12 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
 }
 
 // ---------------------------------------------------------------------------
-// RoPE angle of pair i at position p: p * base^(-2i/rope_dim).  The angle is
-// formed in double and reduced modulo 2*pi with a two-term Cody-Waite split
-// of 2*pi (head = nearest double, tail = the remainder), so positions near
-// 2^20 keep full accuracy; the reduced angle in [-pi, pi] then goes through
-// a single-precision sincos.
+// RoPE rotation of pair i at position p (angle formed and reduced in double,
+// see rope_math.h); the reduced angle goes through a single-precision sincos.
 // ---------------------------------------------------------------------------
-constexpr double kTwoPiHi = 6.283185307179586;
-constexpr double kTwoPiLo = 2.4492935982947064e-16;
-
-__device__ __forceinline__ void rope_cos_sin(int64_t p, int i, int rope_dim, float base,
+__device__ __forceinline__ void rope_cos_sin(int64_t p, int i, int rope_dim, double log2_base,
                                              float* c, float* s) {
-  const double theta = exp2(-2.0 * double(i) / double(rope_dim) * log2(double(base)));
-  const double x = double(p) * theta;
-  const double k = rint(x * (1.0 / kTwoPiHi));
-  double r = fma(-k, kTwoPiHi, x);
-  r = fma(-k, kTwoPiLo, r);
-  sincosf(float(r), s, c);
+  sincosf(float(rope_angle(p, i, rope_dim, log2_base)), s, c);
 }
 
 constexpr float kLog2e = 1.4426950408889634f;

@@ -3,20 +3,30 @@
 // "DeepSeek-V4-Flash 架构：一个 token 的旅程", sections "压缩是逐通道的
 // learned pooling", "一个通道，逐项算出压缩结果" and "压缩条目必须等整组完成后才可见".
 //
-// The work is a bandwidth-bound streaming reduction.  Each lane owns D/64
-// consecutive channels, so every candidate row is one coalesced read of D
-// elements by a wave; the softmax over candidates runs online in registers
-// (running max, running sum, running weighted sum) with several rows in
-// flight; long candidate lists (HCA's 128 rows) are split over up to eight
-// waves whose states merge in LDS; the RMS statistic is one wave reduction;
-// the interleaved RoPE pairs of the trailing slice stay inside a lane.
+// The work is a streaming reduction over the candidate rows of each entry.
+// The fast path gives every lane one channel pair, so a candidate row is one
+// coalesced read per wave, and lays a block's waves out over channel groups
+// and candidate groups, so that a few entries (decode) still occupy every
+// SIMD of their compute units; the softmax over candidates runs on register
+// batches of rows (batch maximum, then one exponential per element), the
+// per-wave states merge in LDS, and RMSNorm and RoPE finish the entry with
+// one pair per thread.  Other widths take a one-wave-per-entry path.
 #include "common.h"
 #include "kernels.h"
 
 namespace csa {
 namespace {
 
-constexpr int kMaxWavesPerEntry = 8;
+constexpr int kMaxWavesPerEntry = 16;
+// Waves per block by channels per lane: wide lanes hold more registers.
+__host__ __device__ constexpr int max_waves(int cpl) { return cpl == 2 ? kMaxWavesPerEntry : 4; }
+constexpr int kMaxSplits = 16;
+
+// Bytes of the split partial states: (max, sum, weighted sum) per channel,
+// slice and entry; the per-entry counters follow, 16-byte aligned.
+__host__ __device__ inline size_t split_part_bytes(int64_t entries, int nsplit, int D) {
+  return (size_t(entries) * nsplit * 3 * D * sizeof(float) + 15) & ~size_t(15);
+}
 
 struct Task {
   int b;
@@ -47,62 +57,55 @@ __device__ __forceinline__ int64_t token_row(const CompressArgs& a, int64_t tok)
   return a.pos == nullptr ? tok - a.tok0 : tok % a.T;
 }
 
+// Fast path: D = 128*gc (gc <= 16).  Lane l of a wave owns the channel
+// pair (2l, 2l+1) of a 128-channel group, so one candidate row is one
+// coalesced 256-byte (bf16) or 512-byte (fp32) read per wave.  The block's
+// gc*gr waves tile (channel group) x (candidate group): a wave runs the
+// softmax over its share of the candidates for its 128 channels, in batches
+// of rows held in registers (the batch maximum first, then one exponential
+// per element; the next batch is in flight meanwhile).  The per-wave
+// (max, sum, weighted sum) states meet in LDS, where every thread of the
+// block merges channels, the RMS statistic is one block reduction, and the
+// RoPE pairs of the trailing slice are rotated with a table built while the
+// first rows were in flight.
 template <int CPL, bool BF16>
-__device__ __forceinline__ void load_lane(const void* base, int64_t off, float (&v)[CPL]) {
-  if constexpr (BF16) {
-    const uint16_t* p = static_cast<const uint16_t*>(base) + off;
-    if constexpr (CPL == 8) {
-      uint4 u = *reinterpret_cast<const uint4*>(p);
-      uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { v[2 * i] = bf16_lo(w[i]); v[2 * i + 1] = bf16_hi(w[i]); }
-    } else if constexpr (CPL == 4) {
-      uint2 u = *reinterpret_cast<const uint2*>(p);
-      v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
-    } else {
-      uint32_t u = *reinterpret_cast<const uint32_t*>(p);
-      v[0] = bf16_lo(u); v[1] = bf16_hi(u);
-    }
-  } else {
-    const float* p = static_cast<const float*>(base) + off;
-#pragma unroll
-    for (int i = 0; i < CPL; i += 2) {
-      float2 f = *reinterpret_cast<const float2*>(p + i);
-      v[i] = f.x; v[i + 1] = f.y;
-    }
-  }
-}
-
-// Fast path: D = 64*CPL, CPL in {2,4,8}.  A block of `wpe` waves builds one
-// entry: the candidate rows are split evenly over the waves, every wave runs
-// the online softmax over its share with four rows in flight at a time, and
-// wave 0 merges the per-wave (max, sum, weighted sum) states through LDS.
-template <int CPL, bool BF16>
-__global__ __launch_bounds__(kWave* kMaxWavesPerEntry) void compress_lanes(CompressArgs a, int wpe) {
-  extern __shared__ float merge[];  // [wpe][3][CPL][64]
-  __shared__ float rope_tab[64 * CPL];  // (cos, sin) of every RoPE pair
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+__global__ __launch_bounds__(kWave* max_waves(CPL)) void compress_lanes(CompressArgs a, int gc, int gr, int nsplit) {
+  extern __shared__ float lds[];  // states [gr][3][D] | y [D] | RoPE (cos, sin) [rope_dim] | partial sums [16]
+  // the wave index is uniform: the candidate and row arithmetic stays scalar
+  const int lane = threadIdx.x % kWave, wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int nthr = blockDim.x;
   const Task task = compress_task(a, blockIdx.x);
   if (!task.live) return;
   const int D = a.D, r = a.ratio, e = task.e;
-  const int c0 = lane * CPL;
+  float* st = lds;
+  float* ybuf = lds + size_t(gr) * 3 * D;
+  float* rope_tab = ybuf + D;
+  float* red = rope_tab + a.rope_dim;
+  const int cg = wave % gc, rg = wave / gc;
+  const int c0 = cg * kWave * CPL + lane * CPL;
   const int64_t seq = int64_t(task.b) * a.in_bstride;
-
-  float m[CPL], s[CPL], acc[CPL];
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) { m[i] = -INFINITY; s[i] = 0.f; acc[i] = 0.f; }
 
   // candidate c: previous-group token (e-1)*r + c for c < cp, else current token
   const int cp = (a.overlap && e > 0) ? r : 0;
   const int C = cp + r;
-  const int per = (C + wpe - 1) / wpe;
-  const int cb = wave * per, ce = min(C, cb + per);
+  // blockIdx.y takes one slice of the candidates; the waves share it out
+  const int cps = (C + nsplit - 1) / nsplit;
+  const int blo = min(C, int(blockIdx.y) * cps), bhi = min(C, blo + cps);
+  const int per = (bhi - blo + gr - 1) / gr;
+  const int cb = min(bhi, blo + rg * per), ce = min(bhi, cb + per);
+  // candidates are consecutive tokens from t_first; their rows follow one
+  // another in the span, or wrap once around the ring (C <= 2r <= T)
+  const int64_t t_first = int64_t(e) * r - cp;
+  const int64_t row_first = a.pos == nullptr ? t_first - a.tok0 : t_first % a.T;
+
   // rows stay in their storage format until absorbed: bf16 pairs or fp32 bits
   constexpr int RW = BF16 ? CPL / 2 : CPL;
-  constexpr int kBatch = BF16 ? 8 : 4;
-  uint32_t g[kBatch][RW], v[kBatch][RW];
-  auto load_raw = [&](const void* base, int64_t off, uint32_t (&w)[RW]) {
-    const uint32_t* p = reinterpret_cast<const uint32_t*>(static_cast<const char*>(base) + off * (BF16 ? 2 : 4));
+  constexpr int kBatch = (BF16 ? 32 : 16) / CPL;
+  uint32_t g0[kBatch][RW], v0[kBatch][RW], g1[kBatch][RW], v1[kBatch][RW];
+  // a row's address is a scalar base (uniform) plus the lane's byte offset
+  constexpr int kEs = BF16 ? 2 : 4;
+  const uint32_t lane_b = uint32_t(c0) * kEs;
+  auto load_raw = [](const char* p, uint32_t (&w)[RW]) {
     if constexpr (RW == 8) {
       const uint4 x = reinterpret_cast<const uint4*>(p)[0], y = reinterpret_cast<const uint4*>(p)[1];
       w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w; w[4] = y.x; w[5] = y.y; w[6] = y.z; w[7] = y.w;
@@ -113,18 +116,10 @@ __global__ __launch_bounds__(kWave* kMaxWavesPerEntry) void compress_lanes(Compr
       const uint2 x = *reinterpret_cast<const uint2*>(p);
       w[0] = x.x; w[1] = x.y;
     } else {
-      w[0] = *p;
+      w[0] = *reinterpret_cast<const uint32_t*>(p);
     }
   };
-  auto elem = [&](const uint32_t (&w)[RW], int i) -> float {
-    if constexpr (BF16) return (i & 1) ? bf16_hi(w[i / 2]) : bf16_lo(w[i / 2]);
-    else return __uint_as_float(w[i]);
-  };
-  // candidates are consecutive tokens from t_first; their rows follow one
-  // another in the span, or wrap once around the ring (C <= 2r <= T)
-  const int64_t t_first = int64_t(e) * r - cp;
-  const int64_t row_first = a.pos == nullptr ? t_first - a.tok0 : t_first % a.T;
-  auto load_batch = [&](int c) {
+  auto load_batch = [&](int c, uint32_t (&g)[kBatch][RW], uint32_t (&v)[kBatch][RW]) {
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       if (c + j < ce) {
@@ -132,101 +127,227 @@ __global__ __launch_bounds__(kWave* kMaxWavesPerEntry) void compress_lanes(Compr
         const bool prev = cc < cp;
         int64_t row = row_first + cc;
         if (a.pos != nullptr && row >= a.T) row -= a.T;
-        const int64_t off = seq + row * D + c0;
-        load_raw(prev ? a.gate_prev : a.gate, off, g[j]);
-        load_raw(prev ? a.kv_prev : a.kv, off, v[j]);
+        const int64_t off = (seq + row * D) * kEs;
+        const char* gp = static_cast<const char*>(prev ? a.gate_prev : a.gate) + off;
+        const char* vp = static_cast<const char*>(prev ? a.kv_prev : a.kv) + off;
+        load_raw(gp + lane_b, g[j]);
+        load_raw(vp + lane_b, v[j]);
       }
     }
   };
-  if (cb < ce) load_batch(cb);
+  auto elem = [&](const uint32_t (&w)[RW], int i) -> float {
+    if constexpr (BF16) return (i & 1) ? bf16_hi(w[i / 2]) : bf16_lo(w[i / 2]);
+    else return __uint_as_float(w[i]);
+  };
+  if (cb < ce) load_batch(cb, g0, v0);
 
-  // RoPE table (one rolled loop, one call site) and gamma while the first
-  // rows are in flight
+  // RoPE table while the first rows are in flight
   const int rope0 = D - a.rope_dim;
-  for (int i = threadIdx.x; i < a.rope_dim / 2; i += blockDim.x)
-    rope_cos_sin(int64_t(e) * r, i, a.rope_dim, a.rope_base, &rope_tab[2 * i], &rope_tab[2 * i + 1]);
-  float gam[CPL];
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) gam[i] = a.gamma[c0 + i];
+  for (int i = threadIdx.x; i < a.rope_dim / 2; i += nthr)
+    rope_cos_sin(int64_t(e) * r, i, a.rope_dim, a.rope_log2_base, &rope_tab[2 * i], &rope_tab[2 * i + 1]);
 
-  for (int c = cb; c < ce; c += kBatch) {
-    if (c != cb) load_batch(c);
+  // running state per channel, the maximum kept in the log2 domain
+  float m[CPL], s[CPL], acc[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) { m[i] = -INFINITY; s[i] = 0.f; acc[i] = 0.f; }
+  auto absorb = [&](int c, const uint32_t (&g)[kBatch][RW], const uint32_t (&v)[kBatch][RW]) {
+    float gf[kBatch][CPL];
+    float mb[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) mb[i] = -INFINITY;
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      if (c + j >= ce) break;
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
-        const float gl = elem(g[j], i) * kLog2e;
-        const float mn = fmaxf(m[i], gl);
-        const float keep = fast_exp2(m[i] - mn);  // 0 on the first candidate
-        const float pj = fast_exp2(gl - mn);
-        s[i] = s[i] * keep + pj;
-        acc[i] = acc[i] * keep + pj * elem(v[j], i);
-        m[i] = mn;
+        gf[j][i] = elem(g[j], i);
+        if (c + j < ce) mb[i] = fmaxf(mb[i], gf[j][i]);
       }
     }
-  }
-  if (wpe > 1) {
-    float* mine = merge + wave * 3 * CPL * kWave;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-      mine[(0 * CPL + i) * kWave + lane] = m[i];
-      mine[(1 * CPL + i) * kWave + lane] = s[i];
-      mine[(2 * CPL + i) * kWave + lane] = acc[i];
+      const float mn = fmaxf(m[i], mb[i] * kLog2e);
+      const float keep = fast_exp2(m[i] - mn);  // 0 while nothing was absorbed
+      s[i] *= keep;
+      acc[i] *= keep;
+      m[i] = mn;
     }
-    __syncthreads();
-    if (wave != 0) return;
-    for (int w = 1; w < wpe; ++w) {
-      const float* o = merge + w * 3 * CPL * kWave;
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const float mw = o[(0 * CPL + i) * kWave + lane];
-        if (mw == -INFINITY) continue;  // that wave had no candidate
-        const float mn = fmaxf(m[i], mw);
-        const float f0 = fast_exp2(m[i] - mn), f1 = fast_exp2(mw - mn);
-        s[i] = s[i] * f0 + o[(1 * CPL + i) * kWave + lane] * f1;
-        acc[i] = acc[i] * f0 + o[(2 * CPL + i) * kWave + lane] * f1;
-        m[i] = mn;
+    for (int j = 0; j < kBatch; ++j) {
+      if (c + j < ce) {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          const float pj = fast_exp2(fmaf(gf[j][i], kLog2e, -m[i]));
+          s[i] += pj;
+          acc[i] = fmaf(pj, elem(v[j], i), acc[i]);
+        }
       }
     }
+  };
+  for (int c = cb; c < ce; c += 2 * kBatch) {
+    if (c + kBatch < ce) load_batch(c + kBatch, g1, v1);
+    absorb(c, g0, v0);
+    if (c + kBatch < ce) {
+      if (c + 2 * kBatch < ce) load_batch(c + 2 * kBatch, g0, v0);
+      absorb(c + kBatch, g1, v1);
+    }
   }
-
-  if (wpe == 1) __syncthreads();  // publishes the RoPE table (merge's barrier does it otherwise)
+  // y: the pooled value of each of the lane's own channels, when the block
+  // has one candidate group (else the block's pooled row goes to LDS)
   float y[CPL];
   float ss = 0.f;
+  if (nsplit == 1 && gr == 1) {
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) { y[i] = acc[i] / s[i]; ss += y[i] * y[i]; }
-  ss = wave_sum(ss);
-  const float inv_rms = rsqrtf(ss / float(D) + a.eps);
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) y[i] *= inv_rms * gam[i];
-  if (c0 + CPL > rope0) {
-#pragma unroll
-    for (int i = 0; i < CPL / 2; ++i) {
-      const int ch = c0 + 2 * i;
-      if (ch < rope0) continue;
-      const float cs = rope_tab[ch - rope0], sn = rope_tab[ch - rope0 + 1];
-      const float x0 = y[2 * i], x1 = y[2 * i + 1];
-      y[2 * i] = x0 * cs - x1 * sn;
-      y[2 * i + 1] = x0 * sn + x1 * cs;
+    for (int i = 0; i < CPL; ++i) {
+      y[i] = acc[i] / s[i];
+      ss = fmaf(y[i], y[i], ss);
     }
+  } else if (nsplit == 1) {
+    {
+      float* mine = st + size_t(rg) * 3 * D + c0;
+#pragma unroll
+      for (int i = 0; i < CPL; i += 2) {
+        *reinterpret_cast<float2*>(mine + i) = float2{m[i], m[i + 1]};
+        *reinterpret_cast<float2*>(mine + D + i) = float2{s[i], s[i + 1]};
+        *reinterpret_cast<float2*>(mine + 2 * D + i) = float2{acc[i], acc[i + 1]};
+      }
+    }
+    __syncthreads();
+    // merge the candidate groups channel by channel
+    for (int c = threadIdx.x; c < D; c += nthr) {
+      float mx = -INFINITY;
+      for (int g = 0; g < gr; ++g) mx = fmaxf(mx, st[size_t(g) * 3 * D + c]);
+      float S = 0.f, A = 0.f;
+      for (int g = 0; g < gr; ++g) {
+        const float* o = st + size_t(g) * 3 * D + c;
+        if (o[0] == -INFINITY) continue;  // that group had no candidate
+        const float f = fast_exp2(o[0] - mx);
+        S = fmaf(o[D], f, S);
+        A = fmaf(o[2 * D], f, A);
+      }
+      const float yc = A / S;
+      ybuf[c] = yc;
+      ss = fmaf(yc, yc, ss);
+    }
+  } else if constexpr (CPL == 2) {
+    // Split entry (one candidate group, a channel pair per lane): publish
+    // this slice's states; the block that arrives last (one counter per
+    // entry) merges every slice and finishes the entry.  Nothing waits on
+    // another block.  The states travel as device-scope stores and loads,
+    // which write through and read past the caches that are private to a
+    // group of compute units; a wave's stores have reached that level once
+    // its store counter drains, and the barrier orders every wave's drain
+    // before thread 0's arrival.  No device-scope fence is needed (here one
+    // would write back or invalidate a whole L2).
+    float* part = static_cast<float*>(a.ws) + size_t(blockIdx.x) * nsplit * 3 * D;
+    unsigned* ctr = reinterpret_cast<unsigned*>(static_cast<char*>(a.ws) + split_part_bytes(gridDim.x, nsplit, D));
+    // one 64-bit device-scope store per state and lane: the lane's channel pair
+    auto st2 = [](float* p, float x0, float x1) {
+      const uint64_t v = uint64_t(__float_as_uint(x0)) | (uint64_t(__float_as_uint(x1)) << 32);
+      __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    float* pp = part + size_t(blockIdx.y) * 3 * D + c0;
+    st2(pp, m[0], m[1]);
+    st2(pp + D, s[0], s[1]);
+    st2(pp + 2 * D, acc[0], acc[1]);
+    __shared__ bool last;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's states are out
+    __syncthreads();
+    if (threadIdx.x == 0)
+      last = __hip_atomic_fetch_add(&ctr[blockIdx.x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             unsigned(nsplit - 1);
+    __syncthreads();
+    if (!last) return;
+    // every lane merges its own channel pair over the slices, all loads at once
+    auto ld2 = [](const float* p) {
+      return __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    uint64_t pm[kMaxSplits], ps[kMaxSplits], pa[kMaxSplits];
+#pragma unroll
+    for (int k = 0; k < kMaxSplits; ++k) {
+      if (k < nsplit) {
+        const float* q = part + size_t(k) * 3 * D + c0;
+        pm[k] = ld2(q);
+        ps[k] = ld2(q + D);
+        pa[k] = ld2(q + 2 * D);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      auto half = [i](uint64_t v) { return __uint_as_float(uint32_t(v >> (32 * i))); };
+      float mx = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < kMaxSplits; ++k)
+        if (k < nsplit) mx = fmaxf(mx, half(pm[k]));
+      float S = 0.f, A = 0.f;
+#pragma unroll
+      for (int k = 0; k < kMaxSplits; ++k) {
+        if (k < nsplit && half(pm[k]) != -INFINITY) {  // slices without candidates hold no state
+          const float f = fast_exp2(half(pm[k]) - mx);
+          S = fmaf(half(ps[k]), f, S);
+          A = fmaf(half(pa[k]), f, A);
+        }
+      }
+      y[i] = A / S;
+      ss = fmaf(y[i], y[i], ss);
+    }
+    if (threadIdx.x == 0)  // every slice has arrived: rearm for the next call
+      __hip_atomic_store(&ctr[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  // RMS over the row: one block reduction (its barrier also publishes the
+  // RoPE table and the pooled row)
+  ss = wave_sum(ss);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  float tot = 0.f;
+  for (int w = 0; w < nthr / kWave; ++w) tot += red[w];
+  const float inv_rms = rsqrtf(tot / float(D) + a.eps);
+  const int64_t o = int64_t(task.b) * a.out_bstride + int64_t(e) * D;
 
-  const int64_t o = int64_t(task.b) * a.out_bstride + int64_t(e) * D + c0;
-  if (a.out_dtype == CSA_BF16) {
-    uint16_t* dst = static_cast<uint16_t*>(a.out) + o;
-    if constexpr (CPL == 8) {
-      uint4 u{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
-      *reinterpret_cast<uint4*>(dst) = u;
-    } else if constexpr (CPL == 4) {
-      *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-    } else {
-      *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(y[0], y[1]);
-    }
-  } else {
-    float* dst = static_cast<float*>(a.out) + o;
+  if (gr == 1) {
+    // the lane's own channels, rotated in place (RoPE pairs never straddle
+    // lanes) and stored with one vector store
 #pragma unroll
-    for (int i = 0; i < CPL; i += 2) *reinterpret_cast<float2*>(dst + i) = float2{y[i], y[i + 1]};
+    for (int i = 0; i < CPL; ++i) y[i] *= inv_rms * a.gamma[c0 + i];
+#pragma unroll
+    for (int i = 0; i < CPL; i += 2) {
+      const int ch = c0 + i;
+      if (ch >= rope0) {
+        const float cs = rope_tab[ch - rope0], sn = rope_tab[ch - rope0 + 1];
+        const float x0 = y[i], x1 = y[i + 1];
+        y[i] = x0 * cs - x1 * sn;
+        y[i + 1] = x0 * sn + x1 * cs;
+      }
+    }
+    if (a.out_dtype == CSA_BF16) {
+      uint32_t* dst = static_cast<uint32_t*>(a.out) + (o + c0) / 2;
+      if constexpr (CPL == 8)
+        *reinterpret_cast<uint4*>(dst) = uint4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
+                                               pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
+      else if constexpr (CPL == 4)
+        *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+      else
+        *dst = pack_bf16x2(y[0], y[1]);
+    } else {
+      float* dst = static_cast<float*>(a.out) + o + c0;
+#pragma unroll
+      for (int i = 0; i < CPL; i += 2) *reinterpret_cast<float2*>(dst + i) = float2{y[i], y[i + 1]};
+    }
+    return;
+  }
+  // scale, rotate the trailing pairs, store one pair per thread
+  for (int q = threadIdx.x; q < D / 2; q += nthr) {
+    const int ch = 2 * q;
+    float y0 = ybuf[ch] * inv_rms * a.gamma[ch], y1 = ybuf[ch + 1] * inv_rms * a.gamma[ch + 1];
+    if (ch >= rope0) {
+      const float cs = rope_tab[ch - rope0], sn = rope_tab[ch - rope0 + 1];
+      const float x0 = y0, x1 = y1;
+      y0 = x0 * cs - x1 * sn;
+      y1 = x0 * sn + x1 * cs;
+    }
+    if (a.out_dtype == CSA_BF16)
+      static_cast<uint32_t*>(a.out)[(o + ch) / 2] = pack_bf16x2(y0, y1);
+    else
+      *reinterpret_cast<float2*>(static_cast<float*>(a.out) + o + ch) = float2{y0, y1};
   }
 }
 
@@ -268,7 +389,7 @@ __global__ __launch_bounds__(kWave) void compress_any(CompressArgs a) {
   const int rope0 = D - a.rope_dim;
   for (int i = lane; i < a.rope_dim / 2; i += kWave) {
     float cs, sn;
-    rope_cos_sin(int64_t(e) * r, i, a.rope_dim, a.rope_base, &cs, &sn);
+    rope_cos_sin(int64_t(e) * r, i, a.rope_dim, a.rope_log2_base, &cs, &sn);
     const float x0 = ybuf[rope0 + 2 * i], x1 = ybuf[rope0 + 2 * i + 1];
     ybuf[rope0 + 2 * i] = x0 * cs - x1 * sn;
     ybuf[rope0 + 2 * i + 1] = x0 * sn + x1 * cs;
@@ -280,27 +401,54 @@ __global__ __launch_bounds__(kWave) void compress_any(CompressArgs a) {
 
 }  // namespace
 
-hipError_t launch_compress(const CompressArgs& a, hipStream_t stream) {
+CompressPlan plan_compress(int64_t entries, int D, int ratio, int overlap) {
+  CompressPlan p{false, 2, 0, 0, 1, 0};
+  if (D % 128 != 0) return p;
+  // Few entries (decode): a channel pair per lane, so that the block's waves
+  // cover the entry's channels and candidates.  Many entries (prefill): as
+  // many channels per lane as divide the row, so that one wave reads whole
+  // rows with 16-byte loads and keeps more bytes in flight.
+  const int wide = D % 512 == 0 ? 8 : (D % 256 == 0 ? 4 : 2);
+  p.cpl = (entries >= 512 || D / 128 > kMaxWavesPerEntry) ? wide : 2;
+  const int gc = D / (kWave * p.cpl);
+  if (gc > max_waves(p.cpl)) return p;
+  p.lanes = true;
+  p.gc = gc;
+  const int64_t cand = int64_t(1 + overlap) * ratio;
+  // Long candidate lists of few entries (the heavily compressed role at
+  // decode) would leave each entry's rows to one compute unit, whose
+  // outstanding reads then bound the time: slice them over blocks, about
+  // eight rows each.
+  if (p.cpl == 2 && cand >= 64 && entries <= 256) p.nsplit = int(cand / 8 < kMaxSplits ? cand / 8 : kMaxSplits);
+  const int64_t cpb = (cand + p.nsplit - 1) / p.nsplit;
+  // candidate groups: spread few entries over all of a block's waves (two
+  // candidates per wave at least); many entries keep their rows together
+  // (a split entry keeps one group per block: its waves publish their
+  // states straight from registers)
+  const int per_min = entries >= 512 ? 8 : 2;
+  int64_t gr = (cpb + per_min - 1) / per_min;
+  const int wmax = max_waves(p.cpl) / gc;
+  gr = gr < 1 ? 1 : (gr > wmax ? wmax : gr);
+  p.gr = p.nsplit > 1 ? 1 : int(gr);
+  if (p.nsplit > 1) p.ws_bytes = split_part_bytes(entries, p.nsplit, D) + ((size_t(entries) * 4 + 15) & ~size_t(15));
+  return p;
+}
+
+hipError_t launch_compress(const CompressArgs& a, const CompressPlan& plan, hipStream_t stream) {
   const int tasks = a.pos == nullptr ? a.B * a.n_entries : a.B;
   if (tasks == 0) return hipSuccess;
-  const int cpl = a.D / kWave;
   auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
   const int in_es = a.in_dtype == CSA_BF16 ? 2 : 4, out_es = a.out_dtype == CSA_BF16 ? 2 : 4;
-  const bool lanes_ok = (a.D % kWave == 0) && (cpl == 2 || cpl == 4 || cpl == 8) && al(a.kv) && al(a.gate) &&
-                        al(a.kv_prev) && al(a.gate_prev) && al(a.out) && (a.in_bstride * in_es) % 16 == 0 &&
-                        (a.out_bstride * out_es) % 16 == 0;
-  if (lanes_ok) {
-    // one wave per 8 candidate rows (one load batch), at most 8 waves
-    const int cand = (1 + a.overlap) * a.ratio;
-    int wpe = (cand + 7) / 8;
-    wpe = wpe < 1 ? 1 : (wpe > kMaxWavesPerEntry ? kMaxWavesPerEntry : wpe);
-    const dim3 grid(tasks), block(kWave * wpe);
-    const size_t lds = wpe > 1 ? size_t(wpe) * 3 * cpl * kWave * sizeof(float) : 0;
+  const bool aligned = al(a.kv) && al(a.gate) && al(a.kv_prev) && al(a.gate_prev) && al(a.out) &&
+                       (a.in_bstride * in_es) % 16 == 0 && (a.out_bstride * out_es) % 16 == 0;
+  if (plan.lanes && aligned) {
+    const dim3 grid(tasks, plan.nsplit), block(kWave * plan.gc * plan.gr);
+    const size_t lds = (size_t(plan.gr) * 3 * a.D + a.D + a.rope_dim + kMaxWavesPerEntry) * sizeof(float);
     const bool bf = a.in_dtype == CSA_BF16;
-#define CSA_COMPRESS_CASE(C)                                                                  \
-  if (cpl == C) {                                                                             \
-    if (bf) hipLaunchKernelGGL((compress_lanes<C, true>), grid, block, lds, stream, a, wpe);  \
-    else hipLaunchKernelGGL((compress_lanes<C, false>), grid, block, lds, stream, a, wpe);    \
+#define CSA_COMPRESS_CASE(C)                                                                                      \
+  if (plan.cpl == C) {                                                                                            \
+    if (bf) hipLaunchKernelGGL((compress_lanes<C, true>), grid, block, lds, stream, a, plan.gc, plan.gr, plan.nsplit); \
+    else hipLaunchKernelGGL((compress_lanes<C, false>), grid, block, lds, stream, a, plan.gc, plan.gr, plan.nsplit);  \
   }
     CSA_COMPRESS_CASE(2)
     CSA_COMPRESS_CASE(4)

@@ -18,14 +18,25 @@ struct CompressArgs {
   int64_t in_bstride;
   int D, ratio, overlap, rope_dim;
   float rope_base, eps;
+  double rope_log2_base;  // log2(rope_base), formed on the host
   int tok0, e0, n_entries;
   const int* pos;  // ring mode when non-null
   void* out;
   int out_dtype;
   int64_t out_bstride;
   int out_cap;
+  void* ws;  // split partials and counters (zero counters on entry, left zero)
 };
-hipError_t launch_compress(const CompressArgs& a, hipStream_t stream);
+// Compressor plan, shared by the workspace-size query and the launch.
+struct CompressPlan {
+  bool lanes;       // D a multiple of 128: the lane kernel (else one wave per entry)
+  int cpl;          // channels per lane (2, 4 or 8)
+  int gc, gr;       // waves per block: channel groups x candidate groups
+  int nsplit;       // blocks per entry (long candidate lists of few entries)
+  size_t ws_bytes;  // split partial states + one arrival counter per entry
+};
+CompressPlan plan_compress(int64_t entries, int D, int ratio, int overlap);
+hipError_t launch_compress(const CompressArgs& a, const CompressPlan& plan, hipStream_t stream);
 
 struct IndexArgs {
   const void* q_idx;
@@ -64,6 +75,7 @@ struct AttnArgs {
   float scale;
   int rope_dim;
   float rope_base;
+  double rope_log2_base;  // log2(rope_base), formed on the host
   int B, S, H, D;
   void* out;
   int out_dtype;

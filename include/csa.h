@@ -92,14 +92,27 @@ int csa_version(void);
  *     entry pos[b]/ratio iff (pos[b]+1) % ratio == 0 (its group just
  *     completed) and that entry is < out_cap; otherwise it writes nothing.
  *     tok0, e0 and n_entries are ignored.  This is the decode-time append.
+ *
+ *   ws, ws_bytes      device workspace of csa_compress_workspace_size(entries,
+ *                     D, ratio, overlap) bytes, entries = B in ring mode and
+ *                     B*n_entries in span mode; 16-byte aligned, caller-owned,
+ *                     may be NULL when that size is 0 (it is non-zero only for
+ *                     long candidate lists of at most 256 entries, whose
+ *                     candidates are split over several workgroups).  It must
+ *                     hold zeros before its first use; every call leaves it
+ *                     ready for the next (its per-entry counters back at zero).
+ *                     Calls that overlap in time must not share one workspace.
+ *                     Returns CSA_ERR_WORKSPACE when too small,
+ *                     CSA_ERR_INVALID_ARG when misaligned.
  */
+size_t csa_compress_workspace_size(int64_t entries, int D, int ratio, int overlap);
 int csa_compress(const void* kv, const void* gate, const void* kv_prev, const void* gate_prev,
                  int in_dtype, const float* gamma,
                  int B, int T, int64_t in_bstride, int D,
                  int ratio, int overlap, int rope_dim, float rope_base, float eps,
                  int tok0, int e0, int n_entries, const int* pos,
                  void* out, int out_dtype, int64_t out_bstride, int out_cap,
-                 hipStream_t stream);
+                 void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * csa_index_score -- indexer scores of every compressed entry.

@@ -54,7 +54,7 @@ def test_status_strings_and_version(lib):
 def _compress(lib, **kw):
     a = dict(kv=P, gate=P, kv_prev=None, gate_prev=None, in_dtype=1, gamma=P, B=1, T=16, in_bstride=16 * 512,
              D=512, ratio=4, overlap=1, rope_dim=64, rope_base=10000.0, eps=1e-6, tok0=0, e0=0, n_entries=4,
-             pos=None, out=P, out_dtype=0, out_bstride=4 * 512, out_cap=4, stream=None)
+             pos=None, out=P, out_dtype=0, out_bstride=4 * 512, out_cap=4, ws=None, ws_bytes=0, stream=None)
     a.update(kw)
     return lib.csa_compress(*a.values())
 
@@ -69,6 +69,22 @@ def _compress(lib, **kw):
 ])
 def test_compress_rejects(lib, bad):
     assert _compress(lib, **bad) == INVALID
+
+
+def test_compress_workspace(lib):
+    # short candidate lists, or many entries: one workgroup per entry, no workspace
+    assert lib.csa_compress_workspace_size(8, 512, 4, 1) == 0
+    assert lib.csa_compress_workspace_size(257, 512, 128, 0) == 0
+    assert lib.csa_compress_workspace_size(4, 100, 128, 0) == 0      # one-wave path
+    # 128 candidates of 4 entries: 16 slices of (max, sum, weighted sum) per channel, then 4 counters
+    need = lib.csa_compress_workspace_size(4, 512, 128, 0)
+    assert need == 4 * 16 * 3 * 512 * 4 + 16
+    assert lib.csa_compress_workspace_size(2, 128, 32, 1) == 2 * 8 * 3 * 128 * 4 + 16
+    long = dict(ratio=128, overlap=0, T=512, in_bstride=512 * 512)
+    assert _compress(lib, **long) == WORKSPACE
+    assert _compress(lib, **long, ws=P, ws_bytes=need - 1) == WORKSPACE
+    assert _compress(lib, **long, ws=ctypes.c_void_p(0x10008), ws_bytes=need) == INVALID
+    assert _compress(lib, **long, ws=P, ws_bytes=need, B=-1) == INVALID
 
 
 def test_compress_rejects_huge_rows(lib):

@@ -79,6 +79,87 @@ def test_compress_span(D, ratio, overlap, rope, T, tok0, e0, n):
         assert np.all(g32[b, :e0] == 7.0) and np.all(g32[b, e0 + n:] == 7.0)
 
 
+@pytest.mark.parametrize("D,in_dtype", [(512, "bf16"), (512, "f32"), (256, "bf16"), (128, "f32"), (640, "bf16")])
+def test_compress_many_entries(D, in_dtype):
+    """Prefill-sized calls (at least 512 entries) read whole rows per wave:
+    eight, four or two channels per lane by the row width, both input
+    dtypes, against the oracle on every entry."""
+    csa = csa_mod()
+    B, n, r = 2, 260, 4
+    T = n * r
+    kv = rows_bf16(61, (B, T, D))
+    gate = rows_bf16(62, (B, T, D))
+    gamma = (1 + 0.1 * np.random.default_rng(63).standard_normal(D)).astype(np.float32)
+    if in_dtype == "bf16":
+        d_kv, d_g = dev_bf16(kv), dev_bf16(gate)
+    else:
+        d_kv, d_g = dev(synth.bf16_to_f64(kv).astype(np.float32)), dev(synth.bf16_to_f64(gate).astype(np.float32))
+    out = torch.zeros((B, n, D), device="cuda")
+    csa.csa_compress(d_kv, d_g, dev(gamma), out, ratio=r, overlap=1, rope_dim=64)
+    torch.cuda.synchronize()
+    got = host(out)
+    for b in range(B):
+        k64, g64 = synth.bf16_to_f64(kv[b]), synth.bf16_to_f64(gate[b])
+        want = np.stack([oracle.compress_entry(e, k64, g64, k64, g64, gamma, r, 1, 64, 10000.0, 1e-6)
+                         for e in range(n)])
+        assert_normwise(got[b], want, what=f"b={b}")
+
+
+@pytest.mark.parametrize("ratio,overlap,D", [(128, 0, 512), (32, 1, 128)])
+def test_compress_split_entries_reuse_workspace(ratio, overlap, D):
+    """Long candidate lists of few entries are sliced over workgroups that
+    merge through a caller-owned workspace: consecutive calls on one
+    workspace (ring mode, where some sequences emit nothing, then span mode)
+    each match the oracle, and the workspace is left ready for reuse."""
+    csa = csa_mod()
+    B, T = 6, 2 * (1 + overlap) * ratio
+    need = csa.csa_compress_workspace_size(B, D, ratio, overlap)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    gamma = (1 + 0.1 * np.random.default_rng(31).standard_normal(D)).astype(np.float32)
+    cap = 6
+    for call, seed in enumerate((41, 43, 47)):
+        kv = rows_bf16(seed, (B, T, D))
+        gate = rows_bf16(seed + 1, (B, T, D))
+        ring = call < 2
+        if ring:
+            # positions: groups that complete (emit) and ones that do not; entry 0 has no previous group
+            pos = np.array([ratio - 1, 2 * ratio - 1, 3 * ratio - 1, ratio + 5, 4 * ratio - 1, 7][:B], np.int32)
+            if call == 1:
+                pos = pos[::-1].copy()
+            out = torch.full((B, cap, D), 3.0, device="cuda")
+            csa.csa_compress(dev_bf16(kv), dev_bf16(gate), dev(gamma), out, ratio=ratio, overlap=overlap,
+                             rope_dim=64, pos=dev(pos), ws=ws)
+        else:
+            out = torch.full((B, cap, D), 3.0, device="cuda")
+            csa.csa_compress(dev_bf16(kv), dev_bf16(gate), dev(gamma), out, ratio=ratio, overlap=overlap,
+                             rope_dim=64, n_entries=1, e0=1, ws=ws)
+        torch.cuda.synchronize()
+        got = host(out)
+        for b in range(B):
+            k64, g64 = synth.bf16_to_f64(kv[b]), synth.bf16_to_f64(gate[b])
+            if ring:
+                p = int(pos[b])
+                if (p + 1) % ratio != 0:
+                    assert np.all(got[b] == 3.0), (call, b)
+                    continue
+                e = p // ratio
+                # the ring holds token t at row t % T: unroll it into absolute token order
+                full_kv = np.zeros((p + 1, D)); full_g = np.zeros((p + 1, D))
+                for t in range(max(0, p + 1 - T), p + 1):
+                    full_kv[t] = k64[t % T]; full_g[t] = g64[t % T]
+            else:
+                e, full_kv, full_g = 1, k64, g64
+            want = oracle.compress_entry(e, full_kv, full_g, full_kv, full_g, gamma, ratio, overlap, 64, 10000.0,
+                                         1e-6)
+            assert_normwise(got[b, e][None], want[None], what=f"call {call} b={b}")
+            rest = np.delete(got[b], e, axis=0)
+            assert np.all(rest == 3.0)
+    # every call rearmed its counters: the tail of the workspace holds zeros again
+    counters = (4 * B + 15) // 16 * 16
+    assert np.all(ws[need - counters:].cpu().numpy() == 0)
+
+
 def test_compress_ring_mode_matches_span_mode_bitwise():
     """Decode-time append (ring of the last 2r tokens, per-sequence position)
     builds the same entries as the prefill span mode, bit for bit."""
