@@ -160,11 +160,10 @@ class DecodeWorkload:
                                    dtype=torch.uint8, device=device)
         torch.cuda.synchronize()
 
-    @property
-    def side_kernels(self):
-        return ("compress_kv",) if self.cfg.csa else ()
-
-    join_before = "sparse_attn"
+    # A decode step stays on one stream: in a replayed graph, a fork to a side
+    # stream and the join before the attention cost more (about 10 us) than
+    # the KV-role compressor they would hide.
+    side_kernels = ()
 
     # the kernels of one step, as (name, callable) in launch order
     def launches(self, c):
@@ -279,7 +278,8 @@ class PrefillWorkload:
                                    dtype=torch.uint8, device=device)
         torch.cuda.synchronize()
 
-    # the KV-role compressor feeds only the attention: it runs beside the index chain
+    # the KV-role compressor feeds only the attention: it runs beside the index
+    # chain (a prefill step is long enough for the fork and join to pay off)
     side_kernels = ("compress_kv",)
     join_before = "sparse_attn"
 
@@ -355,7 +355,7 @@ def _spin(ms):
 
 def run_step(wl, c, only=None, side=None):
     """Enqueue one step.  Kernels the workload marks independent (the KV-role
-    compressor of a CSA decode step, needed only by the attention) go to the
+    compressor of a prefill step, needed only by the attention) go to the
     `side` stream and are joined back before the first kernel that reads them."""
     import torch
     launches = wl.launches(c)
