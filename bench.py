@@ -171,15 +171,16 @@ class DecodeWorkload:
         cfg = self.cfg
         c = c % self.copies
         scale = 1.0 / math.sqrt(cfg.D)
-        L = [("compress_kv", lambda: csa.csa_compress(
-            self.kv_stage, self.gate_stage, self.gamma, self.kv[c], ratio=cfg.ratio, overlap=cfg.overlap,
-            rope_dim=cfg.rope_dim, rope_base=cfg.rope_base, eps=cfg.eps, pos=self.pos, ws=self.ws_ckv))]
+        kv_job = dict(kv=self.kv_stage, gate=self.gate_stage, gamma=self.gamma, out=self.kv[c], ratio=cfg.ratio,
+                      overlap=cfg.overlap, rope_dim=cfg.rope_dim, rope_base=cfg.rope_base, eps=cfg.eps, pos=self.pos,
+                      ws=self.ws_ckv)
         if cfg.csa:
-            L += [
-                ("compress_idx", lambda: csa.csa_compress(
-                    self.ki_stage, self.gi_stage, self.gamma_idx, self.idx_cache[c], ratio=cfg.ratio,
-                    overlap=cfg.overlap, rope_dim=cfg.rope_dim_idx, rope_base=cfg.rope_base, eps=cfg.eps,
-                    pos=self.pos, ws=self.ws_cidx)),
+            # both cache appends (KV entries, index keys) in one compressor launch
+            idx_job = dict(kv=self.ki_stage, gate=self.gi_stage, gamma=self.gamma_idx, out=self.idx_cache[c],
+                           ratio=cfg.ratio, overlap=cfg.overlap, rope_dim=cfg.rope_dim_idx, rope_base=cfg.rope_base,
+                           eps=cfg.eps, pos=self.pos, ws=self.ws_cidx)
+            L = [
+                ("compress", lambda: csa.csa_compress_jobs([kv_job, idx_job])),
                 ("index_score", lambda: csa.csa_index_score(self.q_idx, self.w, self.idx_cache[c], self.pos2,
                                                             self.scores, ratio=cfg.ratio)),
                 ("topk", lambda: csa.csa_topk(self.scores.view(cfg.B, self.Ncap), None, cfg.k,
@@ -189,9 +190,12 @@ class DecodeWorkload:
                     scale=scale, rope_dim=cfg.rope_dim, rope_base=cfg.rope_base, ws=self.ws_attn)),
             ]
         else:
-            L += [("hca_attn", lambda: csa.hca_attn(
-                self.q, self.kv[c], self.win, self.pos2, self.sink, self.out, ratio=cfg.ratio, window=cfg.window,
-                scale=scale, rope_dim=cfg.rope_dim, rope_base=cfg.rope_base, ws=self.ws_attn))]
+            L = [
+                ("compress", lambda: csa.csa_compress(**kv_job)),
+                ("hca_attn", lambda: csa.hca_attn(
+                    self.q, self.kv[c], self.win, self.pos2, self.sink, self.out, ratio=cfg.ratio, window=cfg.window,
+                    scale=scale, rope_dim=cfg.rope_dim, rope_base=cfg.rope_base, ws=self.ws_attn)),
+            ]
         return L
 
     def queries(self):
@@ -208,10 +212,10 @@ class DecodeWorkload:
         rows_in = (1 + cfg.overlap) * cfg.ratio
         vis = self.n_vis
         win = np.minimum(cfg.window, self.pos_np + 1)
-        by = {"compress_kv": emit * (2 * rows_in * D * 2 + D * 2) + D * 4}
+        by = {"compress": emit * (2 * rows_in * D * 2 + D * 2) + D * 4}
         fl = {}
         if cfg.csa:
-            by["compress_idx"] = emit * (2 * rows_in * DI * 2 + DI * 2) + DI * 4
+            by["compress"] += emit * (2 * rows_in * DI * 2 + DI * 2) + DI * 4
             by["index_score"] = int(np.sum(vis * DI * 2) + B * (HI * DI * 2 + HI * 4) + B * self.Ncap * 4)
             fl["index_score"] = int(np.sum(vis) * HI * DI * 2)
             by["topk"] = int(B * self.Ncap * 4 + B * cfg.k * 4)
@@ -542,7 +546,8 @@ def measure(wl, steps, warmup, only=None):
 
 
 KERNEL_SOURCE = {"index_score": "index_score.hip", "topk": "topk.hip", "sparse_attn": "attn.hip",
-                 "hca_attn": "attn.hip", "compress_kv": "compress.hip", "compress_idx": "compress.hip"}
+                 "hca_attn": "attn.hip", "compress": "compress.hip", "compress_kv": "compress.hip",
+                 "compress_idx": "compress.hip"}
 
 
 def measured_traffic(workload, kernel):
@@ -554,7 +559,7 @@ def measured_traffic(workload, kernel):
     import hashlib
     csrc = os.path.join(ROOT, "compressed_sparse_attention_06_amd", "csrc")
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCE[kernel], "common.h", "kernels.h"):
+    for f in (KERNEL_SOURCE[kernel], "common.h", "kernels.h", "rope_math.h"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     for path in glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}.md")):

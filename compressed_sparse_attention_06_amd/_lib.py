@@ -21,6 +21,19 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape or dtype", -3:
 
 _c_int, _c_i64, _c_f, _c_sz, _c_p = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 
+
+class CompressJob(ctypes.Structure):
+    """csa_compress_job of include/csa.h: the arguments of one csa_compress call."""
+    _fields_ = [("kv", _c_p), ("gate", _c_p), ("kv_prev", _c_p), ("gate_prev", _c_p), ("in_dtype", _c_int),
+                ("gamma", _c_p), ("B", _c_int), ("T", _c_int), ("in_bstride", _c_i64), ("D", _c_int),
+                ("ratio", _c_int), ("overlap", _c_int), ("rope_dim", _c_int), ("rope_base", _c_f), ("eps", _c_f),
+                ("tok0", _c_int), ("e0", _c_int), ("n_entries", _c_int), ("pos", _c_p), ("out", _c_p),
+                ("out_dtype", _c_int), ("out_bstride", _c_i64), ("out_cap", _c_int), ("ws", _c_p),
+                ("ws_bytes", _c_sz)]
+
+
+CSA_MAX_COMPRESS_JOBS = 16
+
 # name -> (restype, argtypes); mirrors include/csa.h
 SIGNATURES = {
     "csa_status_string": (ctypes.c_char_p, [_c_int]),
@@ -29,6 +42,7 @@ SIGNATURES = {
     "csa_compress": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_int, _c_p, _c_int, _c_int, _c_i64, _c_int, _c_int, _c_int,
                               _c_int, _c_f, _c_f, _c_int, _c_int, _c_int, _c_p, _c_p, _c_int, _c_i64, _c_int, _c_p,
                               _c_sz, _c_p]),
+    "csa_compress_jobs": (_c_int, [ctypes.POINTER(CompressJob), _c_int, _c_p]),
     "csa_index_score": (_c_int, [_c_p, _c_p, _c_p, _c_int, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                  _c_p, _c_p]),
     "csa_topk_workspace_size": (_c_sz, [_c_int, _c_int, _c_int]),
@@ -114,28 +128,49 @@ def csa_compress_workspace_size(entries, D, ratio, overlap):
     return int(lib().csa_compress_workspace_size(entries, D, ratio, overlap))
 
 
+def _compress_job(kv, gate, gamma, out, *, ratio, overlap, rope_dim, rope_base=10000.0, eps=1e-6,
+                  kv_prev=None, gate_prev=None, tok0=0, e0=0, n_entries=None, pos=None, ws=None):
+    """(CompressJob, tensors it points to) for one compressor call."""
+    B, T, D = kv.shape
+    n = (out.shape[1] - e0) if n_entries is None else n_entries
+    bstride = _rows(kv)
+    for t in (gate, kv_prev, gate_prev):
+        if t is not None and (t.shape != kv.shape or _rows(t) != bstride):
+            raise CsaError("kv, gate, kv_prev and gate_prev must share one layout")
+    _dense(gamma, pos)
+    need = csa_compress_workspace_size(B if pos is not None else B * n, D, ratio, overlap)
+    if need and (ws is None or _bytes(ws) < need):
+        ws = torch.zeros(need, dtype=torch.uint8, device=kv.device)
+    job = CompressJob(_ptr(kv), _ptr(gate), _ptr(kv_prev), _ptr(gate_prev), _dtype(kv), _ptr(gamma), B, T, bstride,
+                      D, ratio, overlap, rope_dim, rope_base, eps, tok0, e0, n, _ptr(pos), _ptr(out), _dtype(out),
+                      _rows(out), out.shape[1], _ptr(ws), _bytes(ws))
+    return job, (kv, gate, gamma, out, kv_prev, gate_prev, pos, ws)
+
+
 def csa_compress(kv, gate, gamma, out, *, ratio, overlap, rope_dim, rope_base=10000.0, eps=1e-6,
                  kv_prev=None, gate_prev=None, tok0=0, e0=0, n_entries=None, pos=None, ws=None, stream=None):
     """kv, gate: [B, T, D] (rows contiguous); out: [B, out_cap, D]; pos: [B] int32 (ring mode) or None.
 
     ws: a zero-filled uint8 device tensor of at least csa_compress_workspace_size bytes (kept by the
     caller across calls, each of which leaves it ready for the next), or None to allocate one."""
-    B, T, D = kv.shape
-    n = (out.shape[1] - e0) if n_entries is None else n_entries
-    need = csa_compress_workspace_size(B if pos is not None else B * n, D, ratio, overlap)
-    if need and (ws is None or _bytes(ws) < need):
-        ws = torch.zeros(need, dtype=torch.uint8, device=kv.device)
-    bstride = _rows(kv)
-    for t in (gate, kv_prev, gate_prev):
-        if t is not None and (t.shape != kv.shape or _rows(t) != bstride):
-            raise CsaError("kv, gate, kv_prev and gate_prev must share one layout")
-    _dense(gamma, pos)
-    st = lib().csa_compress(_ptr(kv), _ptr(gate), _ptr(kv_prev), _ptr(gate_prev), _dtype(kv), _ptr(gamma), B, T,
-                            bstride, D, ratio, overlap, rope_dim, rope_base, eps, tok0, e0, n, _ptr(pos),
-                            _ptr(out), _dtype(out), _rows(out), out.shape[1], _ptr(ws), _bytes(ws),
-                            _stream(stream))
+    j, keep = _compress_job(kv, gate, gamma, out, ratio=ratio, overlap=overlap, rope_dim=rope_dim,
+                            rope_base=rope_base, eps=eps, kv_prev=kv_prev, gate_prev=gate_prev, tok0=tok0, e0=e0,
+                            n_entries=n_entries, pos=pos, ws=ws)
+    st = lib().csa_compress(j.kv, j.gate, j.kv_prev, j.gate_prev, j.in_dtype, j.gamma, j.B, j.T, j.in_bstride, j.D,
+                            j.ratio, j.overlap, j.rope_dim, j.rope_base, j.eps, j.tok0, j.e0, j.n_entries, j.pos,
+                            j.out, j.out_dtype, j.out_bstride, j.out_cap, j.ws, j.ws_bytes, _stream(stream))
     _check(st, "csa_compress")
     return out
+
+
+def csa_compress_jobs(jobs, stream=None):
+    """Independent compressor calls in one launch: `jobs` is a list of dicts holding the keyword
+    arguments of csa_compress (kv, gate, gamma, out, ratio, overlap, rope_dim, ...)."""
+    built = [_compress_job(**j) for j in jobs]
+    arr = (CompressJob * max(1, len(built)))(*[b[0] for b in built])
+    st = lib().csa_compress_jobs(arr, len(built), _stream(stream))
+    _check(st, "csa_compress_jobs")
+    return [j["out"] for j in jobs]
 
 
 def csa_index_score(q_idx, w, idx_cache, pos, scores, *, ratio, stream=None):

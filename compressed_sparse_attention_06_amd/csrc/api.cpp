@@ -39,61 +39,96 @@ size_t csa_compress_workspace_size(int64_t entries, int D, int ratio, int overla
   return csa::plan_compress(entries, D, ratio, overlap).ws_bytes;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Validates one compressor call and fills its kernel arguments and plan.
+int compress_job(const csa_compress_job& j, csa::CompressArgs* out_args, csa::CompressPlan* out_plan) {
+  if (!j.kv || !j.gate || !j.gamma || !j.out) return CSA_ERR_INVALID_ARG;
+  if (!dtype_ok(j.in_dtype) || !dtype_ok(j.out_dtype)) return CSA_ERR_INVALID_ARG;
+  if (j.B < 0 || j.T < 1 || j.D < 1 || j.ratio < 1 || (j.overlap != 0 && j.overlap != 1)) return CSA_ERR_INVALID_ARG;
+  if (j.rope_dim < 0 || j.rope_dim % 2 != 0 || j.rope_dim > j.D) return CSA_ERR_INVALID_ARG;
+  if (!(j.eps >= 0.f) || !std::isfinite(j.eps) || !(j.rope_base > 0.f) || !std::isfinite(j.rope_base))
+    return CSA_ERR_INVALID_ARG;
+  if (j.out_cap < 0 || j.in_bstride < int64_t(j.T) * j.D || j.out_bstride < int64_t(j.out_cap) * j.D)
+    return CSA_ERR_INVALID_ARG;
+  if (j.D > 8192) return CSA_ERR_UNSUPPORTED;
+  if (j.pos == nullptr) {
+    if (j.tok0 < 0 || j.e0 < 0 || j.n_entries < 0 || int64_t(j.e0) + j.n_entries > j.out_cap)
+      return CSA_ERR_INVALID_ARG;
+    if (j.n_entries > 0) {
+      const int64_t lo = (int64_t(j.e0) - ((j.overlap && j.e0 > 0) ? 1 : 0)) * j.ratio;
+      const int64_t hi = (int64_t(j.e0) + j.n_entries) * j.ratio;
+      if (lo < j.tok0 || hi > int64_t(j.tok0) + j.T) return CSA_ERR_INVALID_ARG;
+    }
+  } else {
+    if (int64_t(j.T) < int64_t(1 + j.overlap) * j.ratio) return CSA_ERR_INVALID_ARG;
+  }
+  const int64_t entries = j.pos == nullptr ? int64_t(j.B) * j.n_entries : j.B;
+  if (entries > INT32_MAX) return CSA_ERR_UNSUPPORTED;
+  const csa::CompressPlan plan = csa::plan_compress(entries, j.D, j.ratio, j.overlap);
+  if (plan.ws_bytes > 0 && (j.ws == nullptr || j.ws_bytes < plan.ws_bytes)) return CSA_ERR_WORKSPACE;
+  if (plan.ws_bytes > 0 && !aligned16(j.ws)) return CSA_ERR_INVALID_ARG;
+  csa::CompressArgs a{};
+  a.kv = j.kv;
+  a.gate = j.gate;
+  a.kv_prev = j.kv_prev ? j.kv_prev : j.kv;
+  a.gate_prev = j.gate_prev ? j.gate_prev : j.gate;
+  a.in_dtype = j.in_dtype;
+  a.gamma = j.gamma;
+  a.B = j.B;
+  a.T = j.T;
+  a.in_bstride = j.in_bstride;
+  a.D = j.D;
+  a.ratio = j.ratio;
+  a.overlap = j.overlap;
+  a.rope_dim = j.rope_dim;
+  a.rope_base = j.rope_base;
+  a.rope_log2_base = std::log2(double(j.rope_base));
+  a.eps = j.eps;
+  a.tok0 = j.tok0;
+  a.e0 = j.e0;
+  a.n_entries = j.n_entries;
+  a.pos = j.pos;
+  a.out = j.out;
+  a.out_dtype = j.out_dtype;
+  a.out_bstride = j.out_bstride;
+  a.out_cap = j.out_cap;
+  a.ws = j.ws;
+  *out_args = a;
+  *out_plan = plan;
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int csa_compress(const void* kv, const void* gate, const void* kv_prev, const void* gate_prev, int in_dtype,
                  const float* gamma, int B, int T, int64_t in_bstride, int D, int ratio, int overlap,
                  int rope_dim, float rope_base, float eps, int tok0, int e0, int n_entries, const int* pos,
                  void* out, int out_dtype, int64_t out_bstride, int out_cap, void* ws, size_t ws_bytes,
                  hipStream_t stream) {
-  if (!kv || !gate || !gamma || !out) return CSA_ERR_INVALID_ARG;
-  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return CSA_ERR_INVALID_ARG;
-  if (B < 0 || T < 1 || D < 1 || ratio < 1 || (overlap != 0 && overlap != 1)) return CSA_ERR_INVALID_ARG;
-  if (rope_dim < 0 || rope_dim % 2 != 0 || rope_dim > D) return CSA_ERR_INVALID_ARG;
-  if (!(eps >= 0.f) || !std::isfinite(eps) || !(rope_base > 0.f) || !std::isfinite(rope_base))
-    return CSA_ERR_INVALID_ARG;
-  if (out_cap < 0 || in_bstride < int64_t(T) * D || out_bstride < int64_t(out_cap) * D) return CSA_ERR_INVALID_ARG;
-  if (D > 8192) return CSA_ERR_UNSUPPORTED;
-  if (pos == nullptr) {
-    if (tok0 < 0 || e0 < 0 || n_entries < 0 || int64_t(e0) + n_entries > out_cap) return CSA_ERR_INVALID_ARG;
-    if (n_entries > 0) {
-      const int64_t lo = (int64_t(e0) - ((overlap && e0 > 0) ? 1 : 0)) * ratio;
-      const int64_t hi = (int64_t(e0) + n_entries) * ratio;
-      if (lo < tok0 || hi > int64_t(tok0) + T) return CSA_ERR_INVALID_ARG;
-    }
-  } else {
-    if (int64_t(T) < int64_t(1 + overlap) * ratio) return CSA_ERR_INVALID_ARG;
+  const csa_compress_job j{kv,   gate,  kv_prev, gate_prev, in_dtype, gamma,     B,         T,       in_bstride,
+                           D,    ratio, overlap, rope_dim,  rope_base, eps,      tok0,      e0,      n_entries,
+                           pos,  out,   out_dtype, out_bstride, out_cap, ws,      ws_bytes};
+  csa::CompressArgs a;
+  csa::CompressPlan plan;
+  const int st = compress_job(j, &a, &plan);
+  if (st != CSA_OK) return st;
+  return hip_status(csa::launch_compress(&a, &plan, 1, stream));
+}
+
+int csa_compress_jobs(const csa_compress_job* jobs, int n_jobs, hipStream_t stream) {
+  if (n_jobs < 0 || n_jobs > CSA_MAX_COMPRESS_JOBS || (n_jobs > 0 && jobs == nullptr)) return CSA_ERR_INVALID_ARG;
+  csa::CompressArgs a[CSA_MAX_COMPRESS_JOBS];
+  csa::CompressPlan plan[CSA_MAX_COMPRESS_JOBS];
+  for (int i = 0; i < n_jobs; ++i) {
+    const int st = compress_job(jobs[i], &a[i], &plan[i]);
+    if (st != CSA_OK) return st;
   }
-  const int64_t entries = pos == nullptr ? int64_t(B) * n_entries : B;
-  if (entries > INT32_MAX) return CSA_ERR_UNSUPPORTED;
-  const csa::CompressPlan plan = csa::plan_compress(entries, D, ratio, overlap);
-  if (plan.ws_bytes > 0 && (ws == nullptr || ws_bytes < plan.ws_bytes)) return CSA_ERR_WORKSPACE;
-  if (plan.ws_bytes > 0 && !aligned16(ws)) return CSA_ERR_INVALID_ARG;
-  csa::CompressArgs a{};
-  a.kv = kv;
-  a.gate = gate;
-  a.kv_prev = kv_prev ? kv_prev : kv;
-  a.gate_prev = gate_prev ? gate_prev : gate;
-  a.in_dtype = in_dtype;
-  a.gamma = gamma;
-  a.B = B;
-  a.T = T;
-  a.in_bstride = in_bstride;
-  a.D = D;
-  a.ratio = ratio;
-  a.overlap = overlap;
-  a.rope_dim = rope_dim;
-  a.rope_base = rope_base;
-  a.rope_log2_base = std::log2(double(rope_base));
-  a.eps = eps;
-  a.tok0 = tok0;
-  a.e0 = e0;
-  a.n_entries = n_entries;
-  a.pos = pos;
-  a.out = out;
-  a.out_dtype = out_dtype;
-  a.out_bstride = out_bstride;
-  a.out_cap = out_cap;
-  a.ws = ws;
-  return hip_status(csa::launch_compress(a, plan, stream));
+  return hip_status(csa::launch_compress(a, plan, n_jobs, stream));
 }
 
 int csa_index_score(const void* q_idx, const float* w, const void* idx_cache, int dtype, const int* pos, int B,

@@ -11,6 +11,8 @@
 // batches of rows (batch maximum, then one exponential per element), the
 // per-wave states merge in LDS, and RMSNorm and RoPE finish the entry with
 // one pair per thread.  Other widths take a one-wave-per-entry path.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -21,6 +23,17 @@ constexpr int kMaxWavesPerEntry = 16;
 // Waves per block by channels per lane: wide lanes hold more registers.
 __host__ __device__ constexpr int max_waves(int cpl) { return cpl == 2 ? kMaxWavesPerEntry : 4; }
 constexpr int kMaxSplits = 16;
+constexpr int kMaxJobs = 4;
+
+// Jobs of one launch: blocks [first[j], first[j+1]) build job j's entries,
+// with job j's own plan (its waves per block may be fewer than the launch's:
+// the others idle through the barriers).
+struct CompressBatch {
+  CompressArgs job[kMaxJobs];
+  int first[kMaxJobs + 1];
+  int gc[kMaxJobs], gr[kMaxJobs], nsplit[kMaxJobs];
+  int n;
+};
 
 // Bytes of the split partial states: (max, sum, weighted sum) per channel,
 // slice and entry; the per-entry counters follow, 16-byte aligned.
@@ -69,12 +82,21 @@ __device__ __forceinline__ int64_t token_row(const CompressArgs& a, int64_t tok)
 // RoPE pairs of the trailing slice are rotated with a table built while the
 // first rows were in flight.
 template <int CPL, bool BF16>
-__global__ __launch_bounds__(kWave* max_waves(CPL)) void compress_lanes(CompressArgs a, int gc, int gr, int nsplit) {
+__global__ __launch_bounds__(kWave* max_waves(CPL)) void compress_lanes(CompressBatch batch) {
   extern __shared__ float lds[];  // states [gr][3][D] | y [D] | RoPE (cos, sin) [rope_dim] | partial sums [16]
   // the wave index is uniform: the candidate and row arithmetic stays scalar
   const int lane = threadIdx.x % kWave, wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int nthr = blockDim.x;
-  const Task task = compress_task(a, blockIdx.x);
+  int j = 0;
+  for (int k = 1; k < batch.n; ++k)
+    if (int(blockIdx.x) >= batch.first[k]) j = k;
+  const CompressArgs a = batch.job[j];
+  const int gc = batch.gc[j], gr = batch.gr[j], nsplit = batch.nsplit[j];
+  const int w = int(blockIdx.x) - batch.first[j];           // entry task within the job
+  const int entries = batch.first[j + 1] - batch.first[j];  // the job's entry tasks
+  if (int(blockIdx.y) >= nsplit) return;
+  const bool active = wave < gc * gr;  // else an idle wave of a smaller job
+  const Task task = compress_task(a, w);
   if (!task.live) return;
   const int D = a.D, r = a.ratio, e = task.e;
   float* st = lds;
@@ -198,11 +220,11 @@ __global__ __launch_bounds__(kWave* max_waves(CPL)) void compress_lanes(Compress
   if (nsplit == 1 && gr == 1) {
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-      y[i] = acc[i] / s[i];
+      y[i] = active ? acc[i] / s[i] : 0.f;
       ss = fmaf(y[i], y[i], ss);
     }
   } else if (nsplit == 1) {
-    {
+    if (active) {
       float* mine = st + size_t(rg) * 3 * D + c0;
 #pragma unroll
       for (int i = 0; i < CPL; i += 2) {
@@ -238,8 +260,8 @@ __global__ __launch_bounds__(kWave* max_waves(CPL)) void compress_lanes(Compress
     // its store counter drains, and the barrier orders every wave's drain
     // before thread 0's arrival.  No device-scope fence is needed (here one
     // would write back or invalidate a whole L2).
-    float* part = static_cast<float*>(a.ws) + size_t(blockIdx.x) * nsplit * 3 * D;
-    unsigned* ctr = reinterpret_cast<unsigned*>(static_cast<char*>(a.ws) + split_part_bytes(gridDim.x, nsplit, D));
+    float* part = static_cast<float*>(a.ws) + size_t(w) * nsplit * 3 * D;
+    unsigned* ctr = reinterpret_cast<unsigned*>(static_cast<char*>(a.ws) + split_part_bytes(entries, nsplit, D));
     // one 64-bit device-scope store per state and lane: the lane's channel pair
     auto st2 = [](float* p, float x0, float x1) {
       const uint64_t v = uint64_t(__float_as_uint(x0)) | (uint64_t(__float_as_uint(x1)) << 32);
@@ -253,7 +275,7 @@ __global__ __launch_bounds__(kWave* max_waves(CPL)) void compress_lanes(Compress
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's states are out
     __syncthreads();
     if (threadIdx.x == 0)
-      last = __hip_atomic_fetch_add(&ctr[blockIdx.x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+      last = __hip_atomic_fetch_add(&ctr[w], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
              unsigned(nsplit - 1);
     __syncthreads();
     if (!last) return;
@@ -291,7 +313,7 @@ __global__ __launch_bounds__(kWave* max_waves(CPL)) void compress_lanes(Compress
       ss = fmaf(y[i], y[i], ss);
     }
     if (threadIdx.x == 0)  // every slice has arrived: rearm for the next call
-      __hip_atomic_store(&ctr[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&ctr[w], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   // RMS over the row: one block reduction (its barrier also publishes the
   // RoPE table and the pooled row)
@@ -304,6 +326,7 @@ __global__ __launch_bounds__(kWave* max_waves(CPL)) void compress_lanes(Compress
   const int64_t o = int64_t(task.b) * a.out_bstride + int64_t(e) * D;
 
   if (gr == 1) {
+    if (!active) return;
     // the lane's own channels, rotated in place (RoPE pairs never straddle
     // lanes) and stored with one vector store
 #pragma unroll
@@ -434,30 +457,76 @@ CompressPlan plan_compress(int64_t entries, int D, int ratio, int overlap) {
   return p;
 }
 
-hipError_t launch_compress(const CompressArgs& a, const CompressPlan& plan, hipStream_t stream) {
-  const int tasks = a.pos == nullptr ? a.B * a.n_entries : a.B;
-  if (tasks == 0) return hipSuccess;
-  auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+namespace {
+
+int job_tasks(const CompressArgs& a) { return a.pos == nullptr ? a.B * a.n_entries : a.B; }
+
+bool lanes_ready(const CompressArgs& a, const CompressPlan& p) {
+  auto al = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
   const int in_es = a.in_dtype == CSA_BF16 ? 2 : 4, out_es = a.out_dtype == CSA_BF16 ? 2 : 4;
-  const bool aligned = al(a.kv) && al(a.gate) && al(a.kv_prev) && al(a.gate_prev) && al(a.out) &&
-                       (a.in_bstride * in_es) % 16 == 0 && (a.out_bstride * out_es) % 16 == 0;
-  if (plan.lanes && aligned) {
-    const dim3 grid(tasks, plan.nsplit), block(kWave * plan.gc * plan.gr);
-    const size_t lds = (size_t(plan.gr) * 3 * a.D + a.D + a.rope_dim + kMaxWavesPerEntry) * sizeof(float);
-    const bool bf = a.in_dtype == CSA_BF16;
-#define CSA_COMPRESS_CASE(C)                                                                                      \
-  if (plan.cpl == C) {                                                                                            \
-    if (bf) hipLaunchKernelGGL((compress_lanes<C, true>), grid, block, lds, stream, a, plan.gc, plan.gr, plan.nsplit); \
-    else hipLaunchKernelGGL((compress_lanes<C, false>), grid, block, lds, stream, a, plan.gc, plan.gr, plan.nsplit);  \
+  return p.lanes && al(a.kv) && al(a.gate) && al(a.kv_prev) && al(a.gate_prev) && al(a.out) &&
+         (a.in_bstride * in_es) % 16 == 0 && (a.out_bstride * out_es) % 16 == 0;
+}
+
+hipError_t launch_lanes(const CompressBatch& b, int cpl, bool bf, int waves, int nsplit, size_t lds,
+                        hipStream_t stream) {
+  const dim3 grid(b.first[b.n], nsplit), block(kWave * waves);
+#define CSA_COMPRESS_CASE(C)                                                                 \
+  if (cpl == C) {                                                                            \
+    if (bf) hipLaunchKernelGGL((compress_lanes<C, true>), grid, block, lds, stream, b);      \
+    else hipLaunchKernelGGL((compress_lanes<C, false>), grid, block, lds, stream, b);        \
   }
-    CSA_COMPRESS_CASE(2)
-    CSA_COMPRESS_CASE(4)
-    CSA_COMPRESS_CASE(8)
+  CSA_COMPRESS_CASE(2)
+  CSA_COMPRESS_CASE(4)
+  CSA_COMPRESS_CASE(8)
 #undef CSA_COMPRESS_CASE
-  } else {
-    hipLaunchKernelGGL(compress_any, dim3(tasks), dim3(kWave), a.D * sizeof(float), stream, a);
-  }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_compress(const CompressArgs* jobs, const CompressPlan* plans, int n, hipStream_t stream) {
+  // Jobs on the lane kernel with one block per entry and the same lane layout
+  // and input dtype share a launch (up to kMaxJobs); the rest run alone.
+  bool done[CSA_MAX_COMPRESS_JOBS] = {};
+  for (int i = 0; i < n; ++i) {
+    if (done[i]) continue;
+    done[i] = true;
+    const CompressArgs& a = jobs[i];
+    const CompressPlan& p = plans[i];
+    if (job_tasks(a) == 0) continue;
+    if (!lanes_ready(a, p)) {
+      hipLaunchKernelGGL(compress_any, dim3(job_tasks(a)), dim3(kWave), a.D * sizeof(float), stream, a);
+      const hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+      continue;
+    }
+    CompressBatch b{};
+    int waves = 0;
+    size_t lds = 0;
+    auto add = [&](const CompressArgs& x, const CompressPlan& q) {
+      const int k = b.n++;
+      b.job[k] = x;
+      b.gc[k] = q.gc;
+      b.gr[k] = q.gr;
+      b.nsplit[k] = q.nsplit;
+      b.first[k + 1] = b.first[k] + job_tasks(x);
+      waves = std::max(waves, q.gc * q.gr);
+      lds = std::max(lds, (size_t(q.gr) * 3 * x.D + x.D + x.rope_dim + kMaxWavesPerEntry) * sizeof(float));
+    };
+    add(a, p);
+    if (p.nsplit == 1) {
+      for (int k = i + 1; k < n && b.n < kMaxJobs; ++k) {
+        if (done[k] || job_tasks(jobs[k]) == 0 || !lanes_ready(jobs[k], plans[k])) continue;
+        if (plans[k].nsplit != 1 || plans[k].cpl != p.cpl || jobs[k].in_dtype != a.in_dtype) continue;
+        done[k] = true;
+        add(jobs[k], plans[k]);
+      }
+    }
+    const hipError_t err = launch_lanes(b, p.cpl, a.in_dtype == CSA_BF16, waves, p.nsplit, lds, stream);
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 }  // namespace csa

@@ -36,7 +36,9 @@ struct CompressPlan {
   size_t ws_bytes;  // split partial states + one arrival counter per entry
 };
 CompressPlan plan_compress(int64_t entries, int D, int ratio, int overlap);
-hipError_t launch_compress(const CompressArgs& a, const CompressPlan& plan, hipStream_t stream);
+// Launch independent compressor jobs; jobs that share a lane layout run in
+// one kernel (results identical to one launch per job).
+hipError_t launch_compress(const CompressArgs* jobs, const CompressPlan* plans, int n, hipStream_t stream);
 
 struct IndexArgs {
   const void* q_idx;

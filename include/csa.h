@@ -115,6 +115,48 @@ int csa_compress(const void* kv, const void* gate, const void* kv_prev, const vo
                  void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * csa_compress_jobs -- several independent csa_compress calls, launched
+ * together.
+ *
+ * A decode step appends to two caches (KV entries and index keys), each one
+ * csa_compress call whose time is mostly one chain of memory latencies; run
+ * as one launch, the chains overlap.  Every job holds exactly the arguments
+ * of one csa_compress call (same meaning, same validation, same workspace
+ * rules) and its results are bit-identical to that call's.  Jobs must be
+ * independent: no job may write memory another job reads or writes.
+ *
+ *   jobs     HOST array of n_jobs descriptors (read during the call only)
+ *   n_jobs   0 .. CSA_MAX_COMPRESS_JOBS
+ * Every job is validated before anything is launched: a rejected call
+ * (the first failing job's status) launches nothing.  Jobs that share a
+ * kernel configuration (one workgroup per entry, the same channels per lane
+ * and input dtype) run in one kernel, at most four per kernel; the others run
+ * one kernel each, in order, on `stream`.
+ */
+#define CSA_MAX_COMPRESS_JOBS 16
+typedef struct csa_compress_job {
+  const void* kv;
+  const void* gate;
+  const void* kv_prev;
+  const void* gate_prev;
+  int in_dtype;
+  const float* gamma;
+  int B, T;
+  int64_t in_bstride;
+  int D, ratio, overlap, rope_dim;
+  float rope_base, eps;
+  int tok0, e0, n_entries;
+  const int* pos;
+  void* out;
+  int out_dtype;
+  int64_t out_bstride;
+  int out_cap;
+  void* ws;
+  size_t ws_bytes;
+} csa_compress_job;
+int csa_compress_jobs(const csa_compress_job* jobs, int n_jobs, hipStream_t stream);
+
+/*
  * csa_index_score -- indexer scores of every compressed entry.
  *
  * [V4-Flash walkthrough] "少读 KV 之前，Indexer 仍要给历史打分": H_I heads of

@@ -87,6 +87,44 @@ def test_compress_workspace(lib):
     assert _compress(lib, **long, ws=P, ws_bytes=need, B=-1) == INVALID
 
 
+def test_compress_job_layout_matches_header(tmp_path):
+    """The binding's CompressJob has the size and field offsets of csa_compress_job."""
+    import shutil
+    import subprocess
+    from compressed_sparse_attention_06_amd import build as B
+    from compressed_sparse_attention_06_amd._lib import CompressJob
+    if shutil.which(B.HIPCC) is None and not os.path.exists(B.HIPCC):
+        pytest.skip("hipcc not available")
+    fields = [f for f, _ in CompressJob._fields_]
+    src = "#include <cstdio>\n#include <cstddef>\n#include \"csa.h\"\nint main() {\n"
+    src += '  printf("%zu\\n", sizeof(csa_compress_job));\n'
+    src += "".join(f'  printf("%zu\\n", offsetof(csa_compress_job, {f}));\n' for f in fields) + "  return 0;\n}\n"
+    (tmp_path / "l.cpp").write_text(src)
+    res = subprocess.run([B.HIPCC, "-I", os.path.join(B.ROOT, "include"), str(tmp_path / "l.cpp"), "-o",
+                          str(tmp_path / "l")], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    got = [int(v) for v in subprocess.run([str(tmp_path / "l")], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(CompressJob)
+    assert got[1:] == [getattr(CompressJob, f).offset for f in fields]
+
+
+def test_compress_jobs_validation(lib):
+    from compressed_sparse_attention_06_amd._lib import CompressJob
+    good = dict(kv=P, gate=P, kv_prev=None, gate_prev=None, in_dtype=1, gamma=P, B=1, T=16, in_bstride=16 * 512,
+                D=512, ratio=4, overlap=1, rope_dim=64, rope_base=10000.0, eps=1e-6, tok0=0, e0=0, n_entries=4,
+                pos=None, out=P, out_dtype=0, out_bstride=4 * 512, out_cap=4, ws=None, ws_bytes=0)
+    arr = (CompressJob * 3)(CompressJob(**good), CompressJob(**dict(good, ratio=0)), CompressJob(**good))
+    assert lib.csa_compress_jobs(arr, 0, None) == 0                     # nothing to do
+    assert lib.csa_compress_jobs(arr, -1, None) == INVALID
+    assert lib.csa_compress_jobs(arr, 17, None) == INVALID              # above CSA_MAX_COMPRESS_JOBS
+    assert lib.csa_compress_jobs(None, 2, None) == INVALID
+    assert lib.csa_compress_jobs(arr, 3, None) == INVALID                # job 1 is invalid: nothing launches
+    long = dict(good, ratio=128, overlap=0, T=512, in_bstride=512 * 512)
+    arr2 = (CompressJob * 2)(CompressJob(**good), CompressJob(**long))
+    assert lib.csa_compress_jobs(arr2, 2, None) == WORKSPACE             # the split job lacks its workspace
+
+
 def test_compress_rejects_huge_rows(lib):
     assert _compress(lib, D=8200, rope_dim=64, in_bstride=16 * 8200, out_bstride=4 * 8200) == UNSUPPORTED
 

@@ -160,6 +160,38 @@ def test_compress_split_entries_reuse_workspace(ratio, overlap, D):
     assert np.all(ws[need - counters:].cpu().numpy() == 0)
 
 
+def test_compress_jobs_match_separate_calls_bitwise():
+    """One csa_compress_jobs call (a decode step's KV and index-key appends
+    sharing a kernel, an fp32-input job and a split long-candidate job that
+    each run alone) writes exactly what one csa_compress call per job writes."""
+    csa = csa_mod()
+    B = 5
+    pos = np.array([3, 22, 47, 45, 127], np.int32)
+    gamma512 = dev((1 + 0.1 * np.random.default_rng(71).standard_normal(512)).astype(np.float32))
+    gamma128 = dev((1 + 0.1 * np.random.default_rng(72).standard_normal(128)).astype(np.float32))
+
+    def job(seed, D, r, overlap, gamma, f32=False):
+        T = 2 * (1 + overlap) * r
+        kv, g = dev_bf16(rows_bf16(seed, (B, T, D))), dev_bf16(rows_bf16(seed + 1, (B, T, D)))
+        if f32:
+            kv, g = kv.float(), g.float()
+        return dict(kv=kv, gate=g, gamma=gamma, ratio=r, overlap=overlap, rope_dim=64, pos=dev(pos))
+
+    specs = [job(81, 512, 4, 1, gamma512), job(83, 128, 4, 1, gamma128), job(85, 512, 4, 1, gamma512, f32=True),
+             job(87, 512, 128, 0, gamma512)]
+    outs = []
+    for sp in specs:
+        sp["out"] = torch.full((B, 40, sp["kv"].shape[2]), 9.0, device="cuda")
+        ref = torch.full_like(sp["out"], 9.0)
+        csa.csa_compress(**dict(sp, out=ref))
+        outs.append(ref)
+    csa.csa_compress_jobs(specs)
+    torch.cuda.synchronize()
+    for sp, ref in zip(specs, outs):
+        assert torch.equal(sp["out"], ref)
+        assert not torch.equal(ref, torch.full_like(ref, 9.0))  # something was written
+
+
 def test_compress_ring_mode_matches_span_mode_bitwise():
     """Decode-time append (ring of the last 2r tokens, per-sequence position)
     builds the same entries as the prefill span mode, bit for bit."""
