@@ -378,10 +378,13 @@ def _oracle_attn(q, cmp, win, sink, sel, pos, window, Wcap, scale, rope, hca_rat
     return out
 
 
-@pytest.mark.parametrize("B,S,pos_kind", [(2, 2, "decode"), (1, 600, "prefill")])
-def test_sparse_attn_mfma(B, S, pos_kind):
+@pytest.mark.parametrize("B,S,pos_kind,k", [(2, 2, "decode", 512), (1, 600, "prefill", 512),
+                                             (2, 2, "decode", 1024), (1, 600, "prefill", 1024)])
+def test_sparse_attn_mfma(B, S, pos_kind, k):
+    """Flash's top-512 and the larger variant's top-1024 selections, decode
+    (split path) and prefill (persistent path)."""
     csa = csa_mod()
-    Ncap, k, window, D = 2048, 512, 128, 512
+    Ncap, window, D = 2048, 128, 512
     if pos_kind == "decode":
         pos = np.array([[8191, 50], [1048575, 0]], np.int32)
         Wcap = 128
