@@ -444,11 +444,12 @@ CompressPlan plan_compress(int64_t entries, int D, int ratio, int overlap) {
   // eight rows each.
   if (p.cpl == 2 && cand >= 64 && entries <= 256) p.nsplit = int(cand / 8 < kMaxSplits ? cand / 8 : kMaxSplits);
   const int64_t cpb = (cand + p.nsplit - 1) / p.nsplit;
-  // candidate groups: spread few entries over all of a block's waves (two
-  // candidates per wave at least); many entries keep their rows together
-  // (a split entry keeps one group per block: its waves publish their
-  // states straight from registers)
-  const int per_min = entries >= 512 ? 8 : 2;
+  // candidate groups: at least eight candidates per wave (one register batch;
+  // a CSA entry's eight rows stay in one group, which then finishes in
+  // registers without the LDS merge -- measured faster than spreading two
+  // rows over each of 16 waves); a split entry keeps one group per block,
+  // whose waves publish their states straight from registers
+  const int per_min = 8;
   int64_t gr = (cpb + per_min - 1) / per_min;
   const int wmax = max_waves(p.cpl) / gc;
   gr = gr < 1 ? 1 : (gr > wmax ? wmax : gr);

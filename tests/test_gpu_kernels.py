@@ -105,6 +105,28 @@ def test_compress_many_entries(D, in_dtype):
         assert_normwise(got[b], want, what=f"b={b}")
 
 
+@pytest.mark.parametrize("ratio,n", [(64, 300), (128, 520)])
+def test_compress_grouped_candidates(ratio, n):
+    """Long candidate lists of many entries (too many to slice over
+    workgroups): the candidates are shared out over several wave groups
+    whose states merge in LDS -- channel pairs at 300 entries, eight
+    channels per lane at 520."""
+    csa = csa_mod()
+    B, D = 1, 512
+    T = n * ratio
+    kv = rows_bf16(91, (B, T, D))
+    gate = rows_bf16(92, (B, T, D))
+    gamma = (1 + 0.1 * np.random.default_rng(93).standard_normal(D)).astype(np.float32)
+    assert csa.csa_compress_workspace_size(B * n, D, ratio, 0) == 0
+    out = torch.zeros((B, n, D), device="cuda")
+    csa.csa_compress(dev_bf16(kv), dev_bf16(gate), dev(gamma), out, ratio=ratio, overlap=0, rope_dim=64)
+    torch.cuda.synchronize()
+    k64, g64 = synth.bf16_to_f64(kv[0]), synth.bf16_to_f64(gate[0])
+    want = np.stack([oracle.compress_entry(e, k64, g64, k64, g64, gamma, ratio, 0, 64, 10000.0, 1e-6)
+                     for e in range(n)])
+    assert_normwise(host(out)[0], want, what=f"ratio {ratio}")
+
+
 @pytest.mark.parametrize("ratio,overlap,D", [(128, 0, 512), (32, 1, 128)])
 def test_compress_split_entries_reuse_workspace(ratio, overlap, D):
     """Long candidate lists of few entries are sliced over workgroups that
