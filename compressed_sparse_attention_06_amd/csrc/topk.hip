@@ -50,16 +50,17 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wsum, uint3
   const uint32_t x = wave_incl_scan(v);
   if (lane == kWave - 1) wsum[wave] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t run = 0;
-    for (int i = 0; i < W; ++i) { const uint32_t t = wsum[i]; wsum[i] = run; run += t; }
-    wsum[W] = run;
+  // every thread adds up the (at most 16) wave totals itself: LDS broadcasts
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    const uint32_t t = wsum[i];
+    before += i < wave ? t : 0u;
+    all += t;
   }
-  __syncthreads();
-  const uint32_t ex = wsum[wave] + x - v;
-  *total = wsum[W];
-  __syncthreads();
-  return ex;
+  *total = all;
+  __syncthreads();  // wsum may be reused by the next scan
+  return before + x - v;
 }
 
 struct SelectArgs {
@@ -137,6 +138,25 @@ __global__ __launch_bounds__(THREADS) void topk_select(SelectArgs a) {
         if constexpr (FROM_CAND) iin[t] = -1;
       }
     }
+    // count and score range of the valid keys, straight from the loads (the
+    // staging barrier below publishes them with the keys)
+    {
+      uint32_t ok = 0;
+      float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < ITEMS; ++t) {
+        if (kin[t] != 0u) {
+          const float f = key_value(kin[t]);
+          ++ok;
+          lo = fminf(lo, f);
+          hi = fmaxf(hi, f);
+        }
+      }
+      ok = wave_sum_u32(ok);
+      lo = wave_min(lo);
+      hi = wave_max(hi);
+      if (lane == 0) { wcount[wave] = ok; wlo[wave] = lo; whi[wave] = hi; }
+    }
 #pragma unroll
     for (int t = 0; t < ITEMS; ++t) {
       keys[lds_swizzle(tid + t * THREADS)] = kin[t];
@@ -155,23 +175,8 @@ __global__ __launch_bounds__(THREADS) void topk_select(SelectArgs a) {
       kidx[t] = w.x; kidx[t + 1] = w.y; kidx[t + 2] = w.z; kidx[t + 3] = w.w;
     }
   }
-  uint32_t ok = 0;
-  float lo = INFINITY, hi = -INFINITY;  // score range of the valid keys
-#pragma unroll
-  for (int t = 0; t < ITEMS; ++t) {
-    if (key[t] != 0u) {
-      const float f = key_value(key[t]);
-      ++ok;
-      lo = fminf(lo, f);
-      hi = fmaxf(hi, f);
-    }
-  }
-  ok = wave_sum_u32(ok);
-  lo = wave_min(lo);
-  hi = wave_max(hi);
-  if (lane == 0) { wcount[wave] = ok; wlo[wave] = lo; whi[wave] = hi; }
-  __syncthreads();
   uint32_t n_ok = 0;
+  float lo = INFINITY, hi = -INFINITY;  // score range of the valid keys
 #pragma unroll
   for (int w = 0; w < W; ++w) { n_ok += wcount[w]; lo = fminf(lo, wlo[w]); hi = fmaxf(hi, whi[w]); }
 
@@ -186,9 +191,17 @@ __global__ __launch_bounds__(THREADS) void topk_select(SelectArgs a) {
       const uint32_t x = uint32_t((key_value(key) - lo) * inv);
       return x < 255u ? x : 255u;
     };
+    // each item's bin, kept (packed bytes) for the gather and the radix passes
+    uint32_t binp[(ITEMS + 3) / 4] = {};
 #pragma unroll
-    for (int t = 0; t < ITEMS; ++t)
-      if (key[t] != 0u) atomicAdd(&hist[wave][bin(key[t])], 1u);
+    for (int t = 0; t < ITEMS; ++t) {
+      if (key[t] != 0u) {
+        const uint32_t bt = bin(key[t]);
+        binp[t / 4] |= bt << (8 * (t % 4));
+        atomicAdd(&hist[wave][bt], 1u);
+      }
+    }
+    auto bin_of = [&](int t) { return (binp[t / 4] >> (8 * (t % 4))) & 255u; };
     __syncthreads();
     // one wave scans the bins from the top: lane L covers bins 255-4L .. 252-4L
     if (wave == 0) {
@@ -214,7 +227,7 @@ __global__ __launch_bounds__(THREADS) void topk_select(SelectArgs a) {
     // one LDS atomic per wave and item slot: lanes take consecutive places
 #pragma unroll
     for (int t = 0; t < ITEMS; ++t) {
-      const bool m = key[t] != 0u && bin(key[t]) == sel_bin;
+      const bool m = key[t] != 0u && bin_of(t) == sel_bin;
       const uint64_t bal = __ballot(m);
       if (bal != 0) {
         uint32_t at0 = 0;
@@ -251,7 +264,7 @@ __global__ __launch_bounds__(THREADS) void topk_select(SelectArgs a) {
 #pragma unroll
         for (int t = 0; t < ITEMS; ++t) {
           const uint32_t kk = key[t];
-          if (kk != 0u && (kk & mask) == prefix && bin(kk) == sel_bin)
+          if (kk != 0u && (kk & mask) == prefix && bin_of(t) == sel_bin)
             atomicAdd(&hist[wave][(kk >> shift) & 255u], 1u);
         }
         __syncthreads();
