@@ -661,7 +661,7 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int nsplit) {
 // attn_redo (never for ordinary data).
 // ---------------------------------------------------------------------------
 constexpr int kPMaxQ = 64;               // queries per workgroup
-constexpr int kPCopyRows = kT / 4;       // rows each PV wave copies per tile
+constexpr int kPCopyRows = kT / 8;       // rows each wave copies per tile
 constexpr int kPMaxSel = 1024;           // CSA selections of a query staged in LDS
 constexpr int kPersistMinQueries = 512;  // fewer queries take attn_mfma
 constexpr int kEpiStores = 8 * 4;        // output stores per PV lane when a query ends (one per dim x head tile)
@@ -679,7 +679,7 @@ template <bool HCA>
 __global__ __launch_bounds__(kThreads) void attn_persist(AttnArgs a, int* redo) {
   __shared__ __attribute__((aligned(16))) unsigned char tiles[kBufs][kT * kPitch];
   __shared__ __attribute__((aligned(16))) uint16_t pt[2][kH * kPPitch];
-  __shared__ __attribute__((aligned(4))) uint8_t vmask[kBufs][4];  // [tile buffer][PV wave]: rows 8v + bit
+  __shared__ __attribute__((aligned(4))) uint8_t vmask[kBufs][8];  // [tile buffer][wave]: rows 4w + bit
   __shared__ __attribute__((aligned(16))) int sel[2][HCA ? 1 : kPMaxSel];
   __shared__ float lsum[2][2][kH];  // [query parity][QK row half][head]
   __shared__ int ovf[2][4];         // [query parity][QK wave]
@@ -740,7 +740,6 @@ __global__ __launch_bounds__(kThreads) void attn_persist(AttnArgs a, int* redo) 
 
   const uint32_t lds_tiles = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)&tiles[0][0]));
   const uint32_t lds_sel = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)&sel[0][0]));
-  const int pw = wave - 4;  // PV wave index (copies)
   // selection list of query k -> sel[k & 1] (wave 4 only)
   auto copy_sel = [&](int k) {
     const int* src = a.idx + int64_t(x + k * G) * a.k;
@@ -750,11 +749,13 @@ __global__ __launch_bounds__(kThreads) void attn_persist(AttnArgs a, int* redo) 
       copy_dwords_to_lds(src, uint32_t(i < a.k ? i : 0) * 4u, dst + uint32_t(m * kWave * 4));
     }
   };
-  // copies of stream tile u (tile u.t of query u.c) into buffer u % kBufs
+  // copies of stream tile u (tile u.t of query u.c) into buffer u % kBufs:
+  // wave w copies rows 4w .. 4w+3 (every wave, so that no wave group stalls
+  // on all of a tile's copies)
   auto issue = [&](const Cur& cu, int u) {
-    if (!HCA && pw == 0 && cu.t == 0 && cu.c.k + 1 < nqb) copy_sel(cu.c.k + 1);  // lands before cu's next query
+    if (!HCA && wave == 4 && cu.t == 0 && cu.c.k + 1 < nqb) copy_sel(cu.c.k + 1);  // lands before cu's next query
     const int buf = u % kBufs;
-    const int j = cu.t * kT + pw * kPCopyRows + (lane % kPCopyRows);
+    const int j = cu.t * kT + wave * kPCopyRows + (lane % kPCopyRows);
     int code = -1;  // >= 0 compressed entry, <= -2 window ring slot, -1 none
     if (j < cu.c.n_win) {
       const int slot = cu.c.s0 + j;
@@ -769,15 +770,14 @@ __global__ __launch_bounds__(kThreads) void attn_persist(AttnArgs a, int* redo) 
       }
     }
     const uint64_t ok = __ballot(code != -1);
-    if (lane == 0) vmask[buf][pw] = uint8_t(ok & 0xffu);
+    if (lane == 0) vmask[buf][wave] = uint8_t(ok & 0xfu);
     const uint16_t* win = static_cast<const uint16_t*>(a.win) + int64_t(cu.c.b) * a.Wcap * kD;
     const uint16_t* cmp = static_cast<const uint16_t*>(a.cmp) + int64_t(cu.c.b) * a.Ncap * kD;
     // the query's first head row stands in for a missing candidate (masked, finite)
     const uint16_t* filler = static_cast<const uint16_t*>(a.q) + int64_t(cu.c.qi) * kH * kD;
-    const uint32_t dst = lds_tiles + uint32_t(buf * kT * kPitch + pw * kPCopyRows * kPitch);
-    // rows 8v..8v+3 are flipped iff v is odd, rows 8v+4..8v+7 iff v is even
-    const uint32_t voff_lo = uint32_t(lane ^ ((pw & 1) << 3)) * 16u;
-    const uint32_t voff_hi = uint32_t(lane ^ (((pw & 1) ^ 1) << 3)) * 16u;
+    const uint32_t dst = lds_tiles + uint32_t(buf * kT * kPitch + wave * kPCopyRows * kPitch);
+    // the wave's four rows share one chunk flip (row_flip)
+    const uint32_t voff = uint32_t(lane ^ (row_flip(wave * kPCopyRows) << 3)) * 16u;
     // lane r forms row r's address; each copy reads it back as a scalar pair
     const uint16_t* src = code >= 0 ? cmp + int64_t(code) * kD : (code <= -2 ? win + int64_t(-2 - code) * kD : filler);
     const uint64_t sa = reinterpret_cast<uint64_t>(src);
@@ -785,7 +785,7 @@ __global__ __launch_bounds__(kThreads) void attn_persist(AttnArgs a, int* redo) 
     for (int r = 0; r < kPCopyRows; ++r) {
       const uint64_t ra = uint64_t(uint32_t(__builtin_amdgcn_readlane(uint32_t(sa), r))) |
                           (uint64_t(uint32_t(__builtin_amdgcn_readlane(uint32_t(sa >> 32), r))) << 32);
-      copy_row_to_lds(reinterpret_cast<const void*>(ra), r < 4 ? voff_lo : voff_hi, dst + uint32_t(r * kPitch));
+      copy_row_to_lds(reinterpret_cast<const void*>(ra), voff, dst + uint32_t(r * kPitch));
     }
   };
   const float qk_scale = a.scale * kLog2e;
@@ -804,8 +804,18 @@ __global__ __launch_bounds__(kThreads) void attn_persist(AttnArgs a, int* redo) 
       }
     };
     load_q(first.c.qi);
-    __syncthreads();  // prologue: first selection list
-    __syncthreads();  // prologue: second selection list
+    wait_vmem<0>();  // Q^T in registers before any copy is issued
+    // prologue, in step with the PV waves: first selection list, tile 0,
+    // second selection list, tile 1
+    Cur ci = first;
+    __syncthreads();
+    issue(ci, 0);
+    advance(ci);
+    __syncthreads();
+    if (total > 1) {
+      issue(ci, 1);
+      advance(ci);
+    }
     const int k_base = (rr * 16 + c16) * kPitch + g * 16;
     const int k_off0 = k_base + row_flip(c16) * 128, k_off1 = k_base - row_flip(c16) * 128;
     float m_ref[2], l_sink[2];
@@ -819,6 +829,9 @@ __global__ __launch_bounds__(kThreads) void attn_persist(AttnArgs a, int* redo) 
     bool over = false;
     Cur cq = first;
     for (int s = 0; s <= total; ++s) {
+      // this wave's copies of tile s have landed (only tile s+1's may still fly)
+      if (s + 1 < total) wait_vmem<kPCopyRows>();
+      else wait_vmem<0>();
       __syncthreads();
       if (s == total) break;
       if (cq.t == 0) {
@@ -830,7 +843,9 @@ __global__ __launch_bounds__(kThreads) void attn_persist(AttnArgs a, int* redo) 
         over = false;
       }
       const unsigned char* tile = tiles[s % kBufs];
-      const uint32_t okm = *reinterpret_cast<const uint16_t*>(&vmask[s % kBufs][rr * 2]);  // rows rr*16 + bit
+      // rows rr*16 + bit: the nibbles of waves 4rr .. 4rr+3
+      const uint32_t w4 = *reinterpret_cast<const uint32_t*>(&vmask[s % kBufs][rr * 4]);
+      const uint32_t okm = (w4 & 0xfu) | ((w4 >> 4) & 0xf0u) | ((w4 >> 8) & 0xf00u) | ((w4 >> 12) & 0xf000u);
       floatx4 st[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
       bf16x8 kr[kAheadK + 1];
 #pragma unroll
@@ -848,7 +863,16 @@ __global__ __launch_bounds__(kThreads) void attn_persist(AttnArgs a, int* redo) 
         __builtin_amdgcn_sched_barrier(0);
       }
       const bool last = cq.t == cq.c.nt - 1;
-      if (last && cq.c.k + 1 < nqb) load_q(cq.c.qi + G);  // the next query's Q^T lands during this step
+      if (last && cq.c.k + 1 < nqb) {
+        // the next query's Q^T, completed here (once per query): the copies
+        // issued below then never hold up the next step's products
+        load_q(cq.c.qi + G);
+        wait_vmem<0>();
+      }
+      if (s + 2 < total) {
+        issue(ci, s + 2);
+        advance(ci);
+      }
       uint16_t* pw_t = &pt[s & 1][0];
 #pragma unroll
       for (int ht = 0; ht < 2; ++ht) {
@@ -882,7 +906,7 @@ __global__ __launch_bounds__(kThreads) void attn_persist(AttnArgs a, int* redo) 
     // prologue: query 0's selection list, then tiles 0 and 1 (tile 0 copies
     // query 1's list first)
     Cur ci = first;
-    if (!HCA && pw == 0) copy_sel(0);
+    if (!HCA && wave == 4) copy_sel(0);
     wait_vmem<0>();
     __syncthreads();
     issue(ci, 0);
@@ -893,6 +917,7 @@ __global__ __launch_bounds__(kThreads) void attn_persist(AttnArgs a, int* redo) 
       issue(ci, 1);
       advance(ci);
     }
+    const int pw = wave - 4;  // PV wave index: dims 128 pw .. 128 pw + 127
     const int v_base = (g * 8 + (c16 >> 2)) * kPitch + pw * 256 + (((c16 >> 1) & 1) << 4) + ((c16 & 1) << 3);
     const int f_lo = (g & 1) * 128, f_hi = ((g & 1) ^ 1) * 128;
     const int v_lo0 = v_base + f_lo, v_lo1 = v_base - f_lo;
