@@ -214,6 +214,46 @@ def test_compress_jobs_match_separate_calls_bitwise():
         assert not torch.equal(ref, torch.full_like(ref, 9.0))  # something was written
 
 
+def test_compress_jobs_many_and_mixed():
+    """Sixteen jobs in one call -- more than one kernel takes, ring and span
+    modes mixed, a job with no entry to build (its groups incomplete) and a
+    job with zero entries -- each bit-identical to its own csa_compress call."""
+    csa = csa_mod()
+    rng = np.random.default_rng(101)
+    specs = []
+    for j in range(16):
+        D = [128, 512, 256][j % 3]
+        B = 1 + j % 3
+        r = 4
+        if j % 2 == 0:  # ring mode: positions that complete a group (and, for j = 4, none that do)
+            T = 2 * 2 * r
+            pos = rng.integers(0, 200, B).astype(np.int32)
+            pos = (pos // r) * r + (r - 1) if j != 4 else (pos // r) * r + 1
+            kv, g = dev_bf16(rows_bf16(200 + j, (B, T, D))), dev_bf16(rows_bf16(300 + j, (B, T, D)))
+            spec = dict(kv=kv, gate=g, ratio=r, overlap=1, rope_dim=64, pos=dev(pos.astype(np.int32)))
+            cap = 60
+        else:  # span mode: entries e0 .. e0+n-1 (none for j = 7)
+            n = 0 if j == 7 else 3 + j % 4
+            T = (n + 2) * r
+            kv, g = dev_bf16(rows_bf16(200 + j, (B, T, D))), dev_bf16(rows_bf16(300 + j, (B, T, D)))
+            spec = dict(kv=kv, gate=g, ratio=r, overlap=1, rope_dim=64, n_entries=n, e0=1)
+            cap = n + 2
+        spec["gamma"] = dev((1 + 0.1 * rng.standard_normal(D)).astype(np.float32))
+        spec["out"] = torch.full((B, cap, D), 4.0, device="cuda")
+        specs.append(spec)
+    refs = []
+    for sp in specs:
+        ref = torch.full_like(sp["out"], 4.0)
+        csa.csa_compress(**dict(sp, out=ref))
+        refs.append(ref)
+    csa.csa_compress_jobs(specs)
+    torch.cuda.synchronize()
+    for j, (sp, ref) in enumerate(zip(specs, refs)):
+        assert torch.equal(sp["out"], ref), j
+    assert torch.equal(refs[4], torch.full_like(refs[4], 4.0))  # no group completed
+    assert torch.equal(refs[7], torch.full_like(refs[7], 4.0))  # no entries asked for
+
+
 def test_compress_ring_mode_matches_span_mode_bitwise():
     """Decode-time append (ring of the last 2r tokens, per-sequence position)
     builds the same entries as the prefill span mode, bit for bit."""
