@@ -4,13 +4,14 @@
 // learned pooling", "一个通道，逐项算出压缩结果" and "压缩条目必须等整组完成后才可见".
 //
 // The work is a streaming reduction over the candidate rows of each entry.
-// The fast path gives every lane one channel pair, so a candidate row is one
-// coalesced read per wave, and lays a block's waves out over channel groups
-// and candidate groups, so that a few entries (decode) still occupy every
-// SIMD of their compute units; the softmax over candidates runs on register
-// batches of rows (batch maximum, then one exponential per element), the
-// per-wave states merge in LDS, and RMSNorm and RoPE finish the entry with
-// one pair per thread.  Other widths take a one-wave-per-entry path.
+// The fast path gives every lane 2, 4 or 8 consecutive channels, so a
+// candidate row is one coalesced read per wave, and lays a block's waves out
+// over channel groups and candidate groups; the softmax over candidates runs
+// on register batches of rows (batch maximum, then one exponential per
+// element).  A block with one candidate group finishes its entry in
+// registers; several groups merge in LDS.  Few entries with long candidate
+// lists are sliced over workgroups that merge through a workspace.  Widths
+// that are not a multiple of 128 take a one-wave-per-entry path.
 #include <algorithm>
 
 #include "common.h"
@@ -70,30 +71,32 @@ __device__ __forceinline__ int64_t token_row(const CompressArgs& a, int64_t tok)
   return a.pos == nullptr ? tok - a.tok0 : tok % a.T;
 }
 
-// Fast path: D = 128*gc (gc <= 16).  Lane l of a wave owns the channel
-// pair (2l, 2l+1) of a 128-channel group, so one candidate row is one
-// coalesced 256-byte (bf16) or 512-byte (fp32) read per wave.  The block's
-// gc*gr waves tile (channel group) x (candidate group): a wave runs the
-// softmax over its share of the candidates for its 128 channels, in batches
-// of rows held in registers (the batch maximum first, then one exponential
-// per element; the next batch is in flight meanwhile).  The per-wave
-// (max, sum, weighted sum) states meet in LDS, where every thread of the
-// block merges channels, the RMS statistic is one block reduction, and the
-// RoPE pairs of the trailing slice are rotated with a table built while the
-// first rows were in flight.
+// Fast path: D = 64*CPL*gc.  Lane l of a wave owns channels CPL*l ..
+// CPL*l + CPL-1 of a (64*CPL)-channel group, so one candidate row is one
+// coalesced read per wave.  The block's gc*gr waves tile (channel group) x
+// (candidate group): a wave runs the softmax over its share of the
+// candidates for its channels, in batches of rows held in registers (the
+// batch maximum first, then one exponential per element; the next batch is
+// in flight meanwhile).  With one candidate group the wave's registers hold
+// the pooled values; otherwise the per-wave (max, sum, weighted sum) states
+// meet in LDS and every thread of the block merges channels.  The RMS
+// statistic is one block reduction; the RoPE pairs of the trailing slice are
+// rotated with a table built while the first rows were in flight.
+// blockIdx.x is (job, entry) of the batch, blockIdx.y the candidate slice of
+// a split entry (split entries always take channel pairs, one group).
 template <int CPL, bool BF16>
 __global__ __launch_bounds__(kWave* max_waves(CPL)) void compress_lanes(CompressBatch batch) {
   extern __shared__ float lds[];  // states [gr][3][D] | y [D] | RoPE (cos, sin) [rope_dim] | partial sums [16]
   // the wave index is uniform: the candidate and row arithmetic stays scalar
   const int lane = threadIdx.x % kWave, wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int nthr = blockDim.x;
-  int j = 0;
+  int job = 0;
   for (int k = 1; k < batch.n; ++k)
-    if (int(blockIdx.x) >= batch.first[k]) j = k;
-  const CompressArgs a = batch.job[j];
-  const int gc = batch.gc[j], gr = batch.gr[j], nsplit = batch.nsplit[j];
-  const int w = int(blockIdx.x) - batch.first[j];           // entry task within the job
-  const int entries = batch.first[j + 1] - batch.first[j];  // the job's entry tasks
+    if (int(blockIdx.x) >= batch.first[k]) job = k;
+  const CompressArgs a = batch.job[job];
+  const int gc = batch.gc[job], gr = batch.gr[job], nsplit = batch.nsplit[job];
+  const int w = int(blockIdx.x) - batch.first[job];             // entry task within the job
+  const int entries = batch.first[job + 1] - batch.first[job];  // the job's entry tasks
   if (int(blockIdx.y) >= nsplit) return;
   const bool active = wave < gc * gr;  // else an idle wave of a smaller job
   const Task task = compress_task(a, w);
@@ -321,7 +324,7 @@ __global__ __launch_bounds__(kWave* max_waves(CPL)) void compress_lanes(Compress
   if (lane == 0) red[wave] = ss;
   __syncthreads();
   float tot = 0.f;
-  for (int w = 0; w < nthr / kWave; ++w) tot += red[w];
+  for (int wv = 0; wv < nthr / kWave; ++wv) tot += red[wv];
   const float inv_rms = rsqrtf(tot / float(D) + a.eps);
   const int64_t o = int64_t(task.b) * a.out_bstride + int64_t(e) * D;
 
