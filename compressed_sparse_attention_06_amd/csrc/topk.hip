@@ -348,10 +348,11 @@ void launch_select(const SelectArgs& a, int tile, int R, int nchunks, hipStream_
 
 int tile_for(int64_t len) { return len <= 2048 ? 2048 : (len <= 8192 ? 8192 : kMaxTile); }
 
-// Levels: the first cuts raw rows into chunks of `first` positions (small
-// chunks when there are few rows, so that many workgroups share a row); the
-// following ones reduce candidate lists in kMaxTile chunks; the last one
-// selects from at most kMaxTile positions.
+// Levels: rows longer than one tile are first cut into 8192-position chunks
+// (512-thread workgroups, several per CU: measured faster than one
+// 1024-thread workgroup per 16384 positions); the following levels reduce
+// candidate lists in kMaxTile chunks; the last one selects from at most
+// kMaxTile positions.
 struct Levels {
   int n;
   int64_t len[8];    // positions per row entering level i
@@ -362,7 +363,7 @@ struct Levels {
 Levels levels_of(int R, int N, int k) {
   Levels L{};
   int64_t len = N;
-  const int first = kMaxTile;
+  const int first = N > kMaxTile ? 8192 : kMaxTile;
   while (true) {
     const int tile = L.n == 0 ? (len > first ? first : tile_for(len)) : (len > kMaxTile ? kMaxTile : tile_for(len));
     L.len[L.n] = len;

@@ -153,9 +153,9 @@ def test_topk_validation_and_workspace(lib):
     # rows of at most one 16384-position tile: a single pass, no workspace
     assert lib.csa_topk_workspace_size(8192, 2048, 512) == 0
     assert lib.csa_topk_workspace_size(8, 16384, 512) == 0
-    # longer rows: each 16384-position chunk keeps 512 candidates (two buffers of key + index)
+    # longer rows: each 8192-position chunk keeps 512 candidates (two buffers of key + index)
     need = lib.csa_topk_workspace_size(32, 262144, 512)
-    assert need == 2 * 32 * (262144 // 16384 * 512) * 8
+    assert need == 2 * 32 * (262144 // 8192 * 512) * 8
     assert lib.csa_topk(P, None, 32, 262144, 512, P, P, need - 1, None) == WORKSPACE
     assert lib.csa_topk(P, None, 32, 262144, 512, P, None, need, None) == WORKSPACE
 
