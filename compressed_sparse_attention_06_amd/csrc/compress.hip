@@ -444,8 +444,9 @@ CompressPlan plan_compress(int64_t entries, int D, int ratio, int overlap) {
   // Long candidate lists of few entries (the heavily compressed role at
   // decode) would leave each entry's rows to one compute unit, whose
   // outstanding reads then bound the time: slice them over blocks, about
-  // eight rows each.
-  if (p.cpl == 2 && cand >= 64 && entries <= 256) p.nsplit = int(cand / 8 < kMaxSplits ? cand / 8 : kMaxSplits);
+  // sixteen rows each (measured against 8 and 32: the last block's merge
+  // reads every slice's states).
+  if (p.cpl == 2 && cand >= 64 && entries <= 256) p.nsplit = int(cand / 16 < kMaxSplits ? cand / 16 : kMaxSplits);
   const int64_t cpb = (cand + p.nsplit - 1) / p.nsplit;
   // candidate groups: at least eight candidates per wave (one register batch;
   // a CSA entry's eight rows stay in one group, which then finishes in

@@ -76,10 +76,11 @@ def test_compress_workspace(lib):
     assert lib.csa_compress_workspace_size(8, 512, 4, 1) == 0
     assert lib.csa_compress_workspace_size(257, 512, 128, 0) == 0
     assert lib.csa_compress_workspace_size(4, 100, 128, 0) == 0      # one-wave path
-    # 128 candidates of 4 entries: 16 slices of (max, sum, weighted sum) per channel, then 4 counters
+    # 128 candidates of 4 entries: 8 slices of (max, sum, weighted sum) per channel, then 4 counters
     need = lib.csa_compress_workspace_size(4, 512, 128, 0)
-    assert need == 4 * 16 * 3 * 512 * 4 + 16
-    assert lib.csa_compress_workspace_size(2, 128, 32, 1) == 2 * 8 * 3 * 128 * 4 + 16
+    assert need == 4 * 8 * 3 * 512 * 4 + 16
+    assert lib.csa_compress_workspace_size(2, 128, 32, 1) == 2 * 4 * 3 * 128 * 4 + 16
+    assert lib.csa_compress_workspace_size(1, 512, 1024, 0) == 1 * 16 * 3 * 512 * 4 + 16  # at most 16 slices
     long = dict(ratio=128, overlap=0, T=512, in_bstride=512 * 512)
     assert _compress(lib, **long) == WORKSPACE
     assert _compress(lib, **long, ws=P, ws_bytes=need - 1) == WORKSPACE
