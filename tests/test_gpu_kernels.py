@@ -127,8 +127,8 @@ def test_compress_grouped_candidates(ratio, n):
     assert_normwise(host(out)[0], want, what=f"ratio {ratio}")
 
 
-@pytest.mark.parametrize("ratio,overlap,D", [(128, 0, 512), (32, 1, 128)])
-def test_compress_split_entries_reuse_workspace(ratio, overlap, D):
+@pytest.mark.parametrize("ratio,overlap,D,f32", [(128, 0, 512, False), (32, 1, 128, False), (128, 0, 256, True)])
+def test_compress_split_entries_reuse_workspace(ratio, overlap, D, f32):
     """Long candidate lists of few entries are sliced over workgroups that
     merge through a caller-owned workspace: consecutive calls on one
     workspace (ring mode, where some sequences emit nothing, then span mode)
@@ -140,6 +140,9 @@ def test_compress_split_entries_reuse_workspace(ratio, overlap, D):
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     gamma = (1 + 0.1 * np.random.default_rng(31).standard_normal(D)).astype(np.float32)
     cap = 6
+    def todev(x):  # bf16 rows, or the same values in fp32
+        return dev(synth.bf16_to_f64(x).astype(np.float32)) if f32 else dev_bf16(x)
+
     for call, seed in enumerate((41, 43, 47)):
         kv = rows_bf16(seed, (B, T, D))
         gate = rows_bf16(seed + 1, (B, T, D))
@@ -150,11 +153,11 @@ def test_compress_split_entries_reuse_workspace(ratio, overlap, D):
             if call == 1:
                 pos = pos[::-1].copy()
             out = torch.full((B, cap, D), 3.0, device="cuda")
-            csa.csa_compress(dev_bf16(kv), dev_bf16(gate), dev(gamma), out, ratio=ratio, overlap=overlap,
+            csa.csa_compress(todev(kv), todev(gate), dev(gamma), out, ratio=ratio, overlap=overlap,
                              rope_dim=64, pos=dev(pos), ws=ws)
         else:
             out = torch.full((B, cap, D), 3.0, device="cuda")
-            csa.csa_compress(dev_bf16(kv), dev_bf16(gate), dev(gamma), out, ratio=ratio, overlap=overlap,
+            csa.csa_compress(todev(kv), todev(gate), dev(gamma), out, ratio=ratio, overlap=overlap,
                              rope_dim=64, n_entries=1, e0=1, ws=ws)
         torch.cuda.synchronize()
         got = host(out)
