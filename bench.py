@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="csa_decode_64k", choices=sorted(synth.CONFIGS))
-    ap.add_argument("--extra", default="hca_decode_1m,csa_decode_1m,csa_prefill_8k",
+    ap.add_argument("--extra", default="hca_decode_1m,csa_decode_1m,csa_prefill_8k,csa_decode_64k_k1024",
                     help="comma-separated secondary workloads measured after the main one ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")

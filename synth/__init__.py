@@ -60,8 +60,12 @@ HCA_DECODE_1M = Config("hca_decode_1m", 2, "decode", B=4, ctx=1048576, ratio=128
                        overlap=0, csa=False)
 CSA_PREFILL_8K = Config("csa_prefill_8k", 3, "prefill", B=1, S=8192)
 CSA_DECODE_1M = Config("csa_decode_1m", 4, "decode", B=32, ctx=1048576, ctx_lo=524288)
+# the 64K-context decode with the Pro model's selection width, top-k 1024 ("LLM Atlas:
+# DeepSeek", section 19)
+CSA_DECODE_64K_K1024 = Config("csa_decode_64k_k1024", 5, "decode", B=8, ctx=65536, k=1024)
 
-CONFIGS = {c.name: c for c in (TINY, CSA_DECODE_64K, HCA_DECODE_1M, CSA_PREFILL_8K, CSA_DECODE_1M)}
+CONFIGS = {c.name: c for c in (TINY, CSA_DECODE_64K, HCA_DECODE_1M, CSA_PREFILL_8K, CSA_DECODE_1M,
+                               CSA_DECODE_64K_K1024)}
 
 # tensor ids of the seeded streams
 T_X, T_WKV, T_WG, T_WKI, T_WGI, T_WQ, T_WQI, T_WW = 0, 1, 2, 3, 4, 5, 6, 7

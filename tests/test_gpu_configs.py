@@ -117,6 +117,15 @@ def test_csa_decode_64k():
     assert _check_decode(wl, [0, 3, 7]) <= 1
 
 
+def test_csa_decode_64k_k1024():
+    """The 64K-context decode with the larger model's top-k of 1024."""
+    import bench
+    wl = bench.DecodeWorkload(synth.CSA_DECODE_64K_K1024, "cuda", copies=1)
+    progress("csa_decode_64k_k1024: step")
+    _step(wl)
+    assert _check_decode(wl, [0, 5]) <= 1
+
+
 def test_hca_decode_1m():
     import bench
     wl = bench.DecodeWorkload(synth.HCA_DECODE_1M, "cuda", copies=1)
