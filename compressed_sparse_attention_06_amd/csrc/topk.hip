@@ -71,6 +71,7 @@ struct SelectArgs {
   int in_len;             // raw: N; candidates: entries per row
   int k;
   int nchunks;            // chunks per row at this level (output stride)
+  int vec4;               // raw source: N % 4 == 0 and 16-byte aligned rows
   int* out_idx;           // final: [R, k]
   uint32_t* okey;         // chunked: [R, nchunks*k]
   int* oidx;
@@ -86,6 +87,7 @@ __device__ __forceinline__ int lds_swizzle(int i) { return (((i >> 2) ^ ((i >> 6
 template <int THREADS, int ITEMS, bool FROM_CAND, bool FINAL>
 __global__ __launch_bounds__(THREADS) void topk_select(SelectArgs a) {
   constexpr int M = THREADS * ITEMS;
+  static_assert(ITEMS % 4 == 0, "keys move in 16-byte groups");
   constexpr int W = THREADS / kWave;
   __shared__ __attribute__((aligned(16))) uint32_t keys[M];
   __shared__ __attribute__((aligned(16))) int idxs[FROM_CAND ? M : 1];
@@ -105,14 +107,39 @@ __global__ __launch_bounds__(THREADS) void topk_select(SelectArgs a) {
   for (int i = lane; i < 256; i += kWave) hist[wave][i] = 0;  // own wave's histogram
   if (tid == 0) nlist = 0;
 
-  // Coalesced, straight-line loads (position tid + t*THREADS); the keys then
+  // Coalesced, straight-line loads (position tid + t*THREADS, or four keys
+  // at 4*(tid + j*THREADS) when rows are 16-byte aligned); the keys then
   // pass once through LDS so that every thread owns the contiguous run
   // [tid*ITEMS, tid*ITEMS + ITEMS) in registers for the rest of the kernel.
   {
     uint32_t kin[ITEMS];
     int iin[FROM_CAND ? ITEMS : 1];
     const int64_t rbase = int64_t(row) * a.in_len;
-    if (base < len) {
+    if (a.vec4 && base < len) {
+      // four keys per load: position 4*(tid + j*THREADS) + c; the last
+      // quad of the row bounds the address, the length masks the keys
+      const int64_t last4 = a.in_len - 4;
+#pragma unroll
+      for (int j = 0; j < ITEMS / 4; ++j) {
+        const int64_t p = base + 4 * (tid + j * THREADS);
+        const int64_t q = rbase + (p < last4 ? p : last4);
+        uint4 v;
+        if constexpr (FROM_CAND) {
+          v = *reinterpret_cast<const uint4*>(a.ckey + q);
+          const int4 w = *reinterpret_cast<const int4*>(a.cidx + q);
+          iin[4 * j] = w.x; iin[4 * j + 1] = w.y; iin[4 * j + 2] = w.z; iin[4 * j + 3] = w.w;
+        } else {
+          v = *reinterpret_cast<const uint4*>(a.scores + q);
+        }
+        kin[4 * j] = v.x; kin[4 * j + 1] = v.y; kin[4 * j + 2] = v.z; kin[4 * j + 3] = v.w;
+      }
+#pragma unroll
+      for (int t = 0; t < ITEMS; ++t) {
+        const bool in = base + 4 * (tid + (t / 4) * THREADS) + t % 4 < len;
+        if constexpr (FROM_CAND) kin[t] = in ? kin[t] : 0u;
+        else kin[t] = in ? score_key(__uint_as_float(kin[t])) : 0u;
+      }
+    } else if (base < len) {
       const int64_t last = len - 1;
 #pragma unroll
       for (int t = 0; t < ITEMS; ++t) {
@@ -157,10 +184,20 @@ __global__ __launch_bounds__(THREADS) void topk_select(SelectArgs a) {
       hi = wave_max(hi);
       if (lane == 0) { wcount[wave] = ok; wlo[wave] = lo; whi[wave] = hi; }
     }
+    if (a.vec4) {
 #pragma unroll
-    for (int t = 0; t < ITEMS; ++t) {
-      keys[lds_swizzle(tid + t * THREADS)] = kin[t];
-      if constexpr (FROM_CAND) idxs[lds_swizzle(tid + t * THREADS)] = iin[t];
+      for (int j = 0; j < ITEMS / 4; ++j) {
+        const int at = lds_swizzle(4 * (tid + j * THREADS));
+        *reinterpret_cast<uint4*>(&keys[at]) = uint4{kin[4 * j], kin[4 * j + 1], kin[4 * j + 2], kin[4 * j + 3]};
+        if constexpr (FROM_CAND)
+          *reinterpret_cast<int4*>(&idxs[at]) = int4{iin[4 * j], iin[4 * j + 1], iin[4 * j + 2], iin[4 * j + 3]};
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < ITEMS; ++t) {
+        keys[lds_swizzle(tid + t * THREADS)] = kin[t];
+        if constexpr (FROM_CAND) idxs[lds_swizzle(tid + t * THREADS)] = iin[t];
+      }
     }
   }
   __syncthreads();
@@ -414,9 +451,12 @@ hipError_t launch_topk(const float* scores, const int* n_valid, int R, int N, in
     if (cur < 0) {
       a.scores = scores;
       a.n_valid = n_valid;
+      a.vec4 = N % 4 == 0 && reinterpret_cast<uintptr_t>(scores) % 16 == 0;
     } else {
       a.ckey = key_buf[cur];
       a.cidx = idx_buf[cur];
+      a.vec4 = len % 4 == 0 && reinterpret_cast<uintptr_t>(a.ckey) % 16 == 0 &&
+               reinterpret_cast<uintptr_t>(a.cidx) % 16 == 0;
     }
     if (last) {
       a.out_idx = idx;

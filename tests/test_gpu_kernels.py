@@ -383,6 +383,8 @@ def test_index_score_long_cache_batches(B, S, Ncap):
 @pytest.mark.parametrize("R,N,k,nvalid", [
     (3, 100, 4, None), (5, 2048, 512, "ragged"), (4, 5000, 512, None), (2, 16384, 512, None),
     (3, 40000, 512, "ragged"), (2, 300000, 1024, None), (2, 700, 512, None), (64, 2048, 512, "causal"),
+    # lengths that are not a multiple of four take the one-key loads
+    (3, 101, 4, None), (2, 30001, 512, "ragged"), (2, 20000, 37, None),
 ])
 def test_topk_exact(R, N, k, nvalid):
     csa = csa_mod()
