@@ -165,6 +165,13 @@ __global__ __launch_bounds__(kWave* max_waves(CPL)) void compress_lanes(Compress
     else return __uint_as_float(w[i]);
   };
   if (cb < ce) load_batch(cb, g0, v0);
+  // an unsliced one-group entry's RMSNorm gains travel with its first rows
+  // (read in the epilogue they would be one more round trip after the barrier)
+  float gam[CPL];
+  if (gr == 1 && nsplit == 1 && active) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) gam[i] = a.gamma[c0 + i];
+  }
 
   // RoPE table while the first rows are in flight
   const int rope0 = D - a.rope_dim;
@@ -333,7 +340,7 @@ __global__ __launch_bounds__(kWave* max_waves(CPL)) void compress_lanes(Compress
     // the lane's own channels, rotated in place (RoPE pairs never straddle
     // lanes) and stored with one vector store
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) y[i] *= inv_rms * a.gamma[c0 + i];
+    for (int i = 0; i < CPL; ++i) y[i] *= inv_rms * (nsplit == 1 ? gam[i] : a.gamma[c0 + i]);
 #pragma unroll
     for (int i = 0; i < CPL; i += 2) {
       const int ch = c0 + i;
