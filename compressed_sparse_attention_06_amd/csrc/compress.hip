@@ -165,10 +165,10 @@ __global__ __launch_bounds__(kWave* max_waves(CPL)) void compress_lanes(Compress
     else return __uint_as_float(w[i]);
   };
   if (cb < ce) load_batch(cb, g0, v0);
-  // an unsliced one-group entry's RMSNorm gains travel with its first rows
-  // (read in the epilogue they would be one more round trip after the barrier)
+  // a one-group entry's RMSNorm gains travel with its first rows (read in
+  // the epilogue they would be one more round trip after the merge)
   float gam[CPL];
-  if (gr == 1 && nsplit == 1 && active) {
+  if (gr == 1 && active) {
 #pragma unroll
     for (int i = 0; i < CPL; ++i) gam[i] = a.gamma[c0 + i];
   }
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(kWave* max_waves(CPL)) void compress_lanes(Compress
     // the lane's own channels, rotated in place (RoPE pairs never straddle
     // lanes) and stored with one vector store
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) y[i] *= inv_rms * (nsplit == 1 ? gam[i] : a.gamma[c0 + i]);
+    for (int i = 0; i < CPL; ++i) y[i] *= inv_rms * gam[i];
 #pragma unroll
     for (int i = 0; i < CPL; i += 2) {
       const int ch = c0 + i;
