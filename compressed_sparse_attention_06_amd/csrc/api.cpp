@@ -68,6 +68,15 @@ int compress_job(const csa_compress_job& j, csa::CompressArgs* out_args, csa::Co
   const int64_t entries = j.pos == nullptr ? int64_t(j.B) * j.n_entries : j.B;
   if (entries > INT32_MAX) return CSA_ERR_UNSUPPORTED;
   const csa::CompressPlan plan = csa::plan_compress(entries, j.D, j.ratio, j.overlap);
+  // the lane kernel reads and writes rows with 16-byte accesses: a misaligned
+  // tensor there is rejected rather than sent down a much slower path
+  if (plan.lanes) {
+    const void* kvp = j.kv_prev ? j.kv_prev : j.kv;
+    const void* gp = j.gate_prev ? j.gate_prev : j.gate;
+    if (!aligned16(j.kv) || !aligned16(j.gate) || !aligned16(kvp) || !aligned16(gp) || !aligned16(j.out) ||
+        (j.in_bstride * esize(j.in_dtype)) % 16 != 0 || (j.out_bstride * esize(j.out_dtype)) % 16 != 0)
+      return CSA_ERR_INVALID_ARG;
+  }
   if (plan.ws_bytes > 0 && (j.ws == nullptr || j.ws_bytes < plan.ws_bytes)) return CSA_ERR_WORKSPACE;
   if (plan.ws_bytes > 0 && !aligned16(j.ws)) return CSA_ERR_INVALID_ARG;
   csa::CompressArgs a{};
@@ -136,8 +145,10 @@ int csa_index_score(const void* q_idx, const float* w, const void* idx_cache, in
   if (!q_idx || !w || !idx_cache || !pos || !scores) return CSA_ERR_INVALID_ARG;
   if (!dtype_ok(dtype) || B < 0 || S < 0 || H_I < 1 || D_I < 1 || Ncap < 0 || ratio < 1) return CSA_ERR_INVALID_ARG;
   if (int64_t(B) * S > INT32_MAX || (int64_t(Ncap) + 255) / 256 > kMaxGridY) return CSA_ERR_UNSUPPORTED;
-  const bool mfma = dtype == CSA_BF16 && H_I == 64 && D_I == 128 && aligned16(q_idx) && aligned16(idx_cache) &&
-                    aligned16(scores);  // the matrix-core kernels store scores in 16-byte groups
+  // matrix-core shape: 16-byte operand loads and score stores in 16-byte
+  // groups, so misaligned tensors are rejected (not run on the vector path)
+  const bool mfma = dtype == CSA_BF16 && H_I == 64 && D_I == 128;
+  if (mfma && !(aligned16(q_idx) && aligned16(idx_cache) && aligned16(scores))) return CSA_ERR_INVALID_ARG;
   if (!mfma && int64_t(H_I) * D_I + H_I > 16384) return CSA_ERR_UNSUPPORTED;
   csa::IndexArgs a{};
   a.q_idx = q_idx;
@@ -189,8 +200,10 @@ int attn_common(const void* q, const void* cmp, int Ncap, const int* idx, int k,
   const int64_t max_cand = int64_t(window) + (hca ? Ncap : k);
   if (max_cand > INT32_MAX) return CSA_ERR_UNSUPPORTED;
   csa::AttnPlan plan = csa::plan_attn(B, S, H, D, window, hca ? Ncap : k, dtype, hca);
+  // matrix-core shape: rows travel in 16-byte pieces, so misaligned tensors
+  // are rejected (not run on the vector path)
   if (plan.mfma && !(aligned16(q) && aligned16(cmp) && (window == 0 || aligned16(win)) && aligned16(out)))
-    plan = csa::AttnPlan{false, false, 1, 0, 0};
+    return CSA_ERR_INVALID_ARG;
   if (!plan.mfma && D > 1024) return CSA_ERR_UNSUPPORTED;
   if (plan.nsplit > kMaxGridY) return CSA_ERR_UNSUPPORTED;
   if (plan.ws_bytes > 0 && (ws == nullptr || ws_bytes < plan.ws_bytes)) return CSA_ERR_WORKSPACE;

@@ -36,10 +36,15 @@ struct CompressBatch {
   int n;
 };
 
-// Bytes of the split partial states: (max, sum, weighted sum) per channel,
-// slice and entry; the per-entry counters follow, 16-byte aligned.
-__host__ __device__ inline size_t split_part_bytes(int64_t entries, int nsplit, int D) {
-  return (size_t(entries) * nsplit * 3 * D * sizeof(float) + 15) & ~size_t(15);
+// Split-entry workspace: one arrival counter per entry slot in a fixed block
+// of kSplitMaxEntries counters at offset 0, then the partial states (max,
+// sum, weighted sum) per channel, slice and entry.  The counters sit at the
+// same place whatever the call's entry count, width or ratio, so a
+// workspace kept across calls of different shapes always finds them zero.
+constexpr int kSplitMaxEntries = 256;
+constexpr size_t kSplitCounterBytes = kSplitMaxEntries * sizeof(unsigned);
+__host__ __device__ inline size_t split_ws_bytes(int64_t entries, int nsplit, int D) {
+  return kSplitCounterBytes + size_t(entries) * nsplit * 3 * D * sizeof(float);
 }
 
 struct Task {
@@ -270,8 +275,8 @@ __global__ __launch_bounds__(kWave* max_waves(CPL)) void compress_lanes(Compress
     // its store counter drains, and the barrier orders every wave's drain
     // before thread 0's arrival.  No device-scope fence is needed (here one
     // would write back or invalidate a whole L2).
-    float* part = static_cast<float*>(a.ws) + size_t(w) * nsplit * 3 * D;
-    unsigned* ctr = reinterpret_cast<unsigned*>(static_cast<char*>(a.ws) + split_part_bytes(entries, nsplit, D));
+    unsigned* ctr = static_cast<unsigned*>(a.ws);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(a.ws) + kSplitCounterBytes) + size_t(w) * nsplit * 3 * D;
     // one 64-bit device-scope store per state and lane: the lane's channel pair
     auto st2 = [](float* p, float x0, float x1) {
       const uint64_t v = uint64_t(__float_as_uint(x0)) | (uint64_t(__float_as_uint(x1)) << 32);
@@ -453,7 +458,7 @@ CompressPlan plan_compress(int64_t entries, int D, int ratio, int overlap) {
   // outstanding reads then bound the time: slice them over blocks, about
   // sixteen rows each (measured against 8 and 32: the last block's merge
   // reads every slice's states).
-  if (p.cpl == 2 && cand >= 64 && entries <= 256) p.nsplit = int(cand / 16 < kMaxSplits ? cand / 16 : kMaxSplits);
+  if (p.cpl == 2 && cand >= 64 && entries <= kSplitMaxEntries) p.nsplit = int(cand / 16 < kMaxSplits ? cand / 16 : kMaxSplits);
   const int64_t cpb = (cand + p.nsplit - 1) / p.nsplit;
   // candidate groups: at least eight candidates per wave (one register batch;
   // a CSA entry's eight rows stay in one group, which then finishes in
@@ -465,7 +470,7 @@ CompressPlan plan_compress(int64_t entries, int D, int ratio, int overlap) {
   const int wmax = max_waves(p.cpl) / gc;
   gr = gr < 1 ? 1 : (gr > wmax ? wmax : gr);
   p.gr = p.nsplit > 1 ? 1 : int(gr);
-  if (p.nsplit > 1) p.ws_bytes = split_part_bytes(entries, p.nsplit, D) + ((size_t(entries) * 4 + 15) & ~size_t(15));
+  if (p.nsplit > 1) p.ws_bytes = split_ws_bytes(entries, p.nsplit, D);
   return p;
 }
 

@@ -19,7 +19,10 @@
  *     allocates, frees or synchronises; all work is enqueued on `stream`
  *     (NULL = the default stream) in call order.
  *   - Tensors are dense, row-major, innermost dimension contiguous, 16-byte
- *     aligned.  bf16 tensors hold raw bfloat16 bit patterns.
+ *     aligned.  bf16 tensors hold raw bfloat16 bit patterns.  On the shapes
+ *     that run the matrix-core or lane kernels (named at each entry point) a
+ *     tensor that is not 16-byte aligned is rejected with
+ *     CSA_ERR_INVALID_ARG; it is never sent down a slower path.
  *   - dtype codes: CSA_F32 (float32) and CSA_BF16 (bfloat16).  Weights w,
  *     sink, gamma and scores are always float32.  Arithmetic is float32
  *     (bf16 x bf16 products accumulate in float32 on the matrix cores).
@@ -98,12 +101,19 @@ int csa_version(void);
  *                     B*n_entries in span mode; 16-byte aligned, caller-owned,
  *                     may be NULL when that size is 0 (it is non-zero only for
  *                     long candidate lists of at most 256 entries, whose
- *                     candidates are split over several workgroups).  It must
- *                     hold zeros before its first use; every call leaves it
- *                     ready for the next (its per-entry counters back at zero).
- *                     Calls that overlap in time must not share one workspace.
+ *                     candidates are split over several workgroups).  Its
+ *                     first 1 KiB holds 256 per-entry arrival counters at a
+ *                     fixed place for every call shape; the partial states
+ *                     follow.  It must hold zeros before its first use; every
+ *                     call leaves the counters back at zero, so one workspace
+ *                     of the largest size needed may serve calls of any batch,
+ *                     width and ratio in turn.  Calls that overlap in time
+ *                     must not share one workspace.
  *                     Returns CSA_ERR_WORKSPACE when too small,
  *                     CSA_ERR_INVALID_ARG when misaligned.
+ *   Lane kernel (D a multiple of 128): kv, gate, kv_prev, gate_prev and out
+ *   must be 16-byte aligned and their sequence strides a multiple of 16
+ *   bytes, else CSA_ERR_INVALID_ARG.
  */
 size_t csa_compress_workspace_size(int64_t entries, int D, int ratio, int overlap);
 int csa_compress(const void* kv, const void* gate, const void* kv_prev, const void* gate_prev,
@@ -170,8 +180,9 @@ int csa_compress_jobs(const csa_compress_job* jobs, int n_jobs, hipStream_t stre
  *   q_idx     [B, S, H_I, D_I] (dtype);  w [B, S, H_I] float32
  *   idx_cache [B, Ncap, D_I]   (dtype);  pos [B, S] int32
  *   scores    [B, S, Ncap]     float32 (written in full)
- * Matrix-core path: dtype CSA_BF16, H_I == 64, D_I == 128.  Other shapes run
- * a vector-ALU path (D_I <= 1024, H_I <= 1024).
+ * Matrix-core path: dtype CSA_BF16, H_I == 64, D_I == 128; q_idx, idx_cache
+ * and scores must then be 16-byte aligned (else CSA_ERR_INVALID_ARG).  Other
+ * shapes run a vector-ALU path (D_I <= 1024, H_I <= 1024).
  */
 int csa_index_score(const void* q_idx, const float* w, const void* idx_cache, int dtype,
                     const int* pos, int B, int S, int H_I, int D_I, int Ncap, int ratio,
@@ -217,8 +228,9 @@ int csa_topk(const float* scores, const int* n_valid, int R, int N, int k, int* 
  *   win [B,Wcap,D] (dtype), pos [B,S] int32, sink [H] float32,
  *   out [B,S,H,D] (out_dtype).  A prefill passes its per-token window rows
  *   with Wcap >= the largest position + 1.
- * Matrix-core path: dtype CSA_BF16, H == 64, D == 512.  Other shapes run a
- * vector-ALU path (D <= 1024).  ws: csa_sparse_attn_workspace_size bytes,
+ * Matrix-core path: dtype CSA_BF16, H == 64, D == 512; q, cmp, win and out
+ * must then be 16-byte aligned (else CSA_ERR_INVALID_ARG).  Other shapes run
+ * a vector-ALU path (D <= 1024).  ws: csa_sparse_attn_workspace_size bytes,
  * 16-byte aligned, caller-owned (device memory; may be null when the size
  * is 0): split partials for few queries, one recompute flag per query for
  * many.  Returns CSA_ERR_WORKSPACE when too small, CSA_ERR_INVALID_ARG when

@@ -76,11 +76,14 @@ def test_compress_workspace(lib):
     assert lib.csa_compress_workspace_size(8, 512, 4, 1) == 0
     assert lib.csa_compress_workspace_size(257, 512, 128, 0) == 0
     assert lib.csa_compress_workspace_size(4, 100, 128, 0) == 0      # one-wave path
-    # 128 candidates of 4 entries: 8 slices of (max, sum, weighted sum) per channel, then 4 counters
+    # 128 candidates of 4 entries: a fixed block of 256 arrival counters (the
+    # same offset for every call shape), then 8 slices of (max, sum, weighted
+    # sum) per channel and entry
     need = lib.csa_compress_workspace_size(4, 512, 128, 0)
-    assert need == 4 * 8 * 3 * 512 * 4 + 16
-    assert lib.csa_compress_workspace_size(2, 128, 32, 1) == 2 * 4 * 3 * 128 * 4 + 16
-    assert lib.csa_compress_workspace_size(1, 512, 1024, 0) == 1 * 16 * 3 * 512 * 4 + 16  # at most 16 slices
+    assert need == 1024 + 4 * 8 * 3 * 512 * 4
+    assert lib.csa_compress_workspace_size(2, 128, 32, 1) == 1024 + 2 * 4 * 3 * 128 * 4
+    assert lib.csa_compress_workspace_size(1, 512, 1024, 0) == 1024 + 1 * 16 * 3 * 512 * 4  # at most 16 slices
+    assert lib.csa_compress_workspace_size(256, 512, 128, 0) == 1024 + 256 * 8 * 3 * 512 * 4
     long = dict(ratio=128, overlap=0, T=512, in_bstride=512 * 512)
     assert _compress(lib, **long) == WORKSPACE
     assert _compress(lib, **long, ws=P, ws_bytes=need - 1) == WORKSPACE
@@ -192,3 +195,23 @@ def test_attn_workspace_sizes(lib):
     assert lib.hca_attn(P, P, 8192, 0, P, 128, 128, P, P, 1, 0.04, 64, 1e4, 4, 1, 64, 512, P, 0, P, hws, None) == INVALID
     assert lib.hca_attn(P, P, 8192, 128, P, 128, 128, P, P, 1, 0.04, 64, 1e4, 4, 1, 64, 512, P, 0, P, hws - 1,
                         None) == WORKSPACE
+
+
+MIS = ctypes.c_void_p(0x10008)  # 8-byte but not 16-byte aligned
+
+
+def test_misaligned_fast_shapes_are_rejected(lib):
+    """The header requires 16-byte aligned tensors; on the matrix-core and
+    lane-kernel shapes a misaligned pointer is an invalid argument (no slower
+    fallback)."""
+    for key in ("kv", "gate", "out", "kv_prev", "gate_prev"):
+        assert _compress(lib, **{key: MIS}) == INVALID, key
+    assert _compress(lib, in_bstride=16 * 512 + 4) == INVALID        # sequence starts off 16 bytes
+    assert _compress(lib, out_bstride=4 * 512 + 2) == INVALID        # fp32 output: 8,200-byte stride
+    for key in ("q", "cache", "scores"):
+        assert _index(lib, **{key: MIS}) == INVALID, key
+    for key in ("q", "cmp", "win", "out"):
+        assert _attn(lib, **{key: MIS}) == INVALID, key
+    hws = lib.hca_attn_workspace_size(4, 1, 64, 512, 8192, 128)
+    assert lib.hca_attn(MIS, P, 8192, 128, P, 128, 128, P, P, 1, 0.04, 64, 1e4, 4, 1, 64, 512, P, 0, P, hws,
+                        None) == INVALID

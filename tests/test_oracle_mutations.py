@@ -12,7 +12,7 @@ from tests import test_oracle_attention as A
 from tests import test_oracle_pins as P
 
 _orig = {name: getattr(csa, name) for name in ("pool", "rope", "rms_norm", "index_score", "topk", "attend",
-                                                "window_positions", "sparse_attn")}
+                                                "window_positions", "sparse_attn", "entry_from_rows")}
 
 
 def _pool_wrong_axis(gates, values):
@@ -46,6 +46,22 @@ def _rope_half_split(x, pos, rope_dim, base=10000.0, inverse=False):
     x[..., d - rope_dim:d - h] = lo * c - hi * s
     x[..., d - h:] = lo * s + hi * c
     return x
+
+
+def _entry_rope_before_norm(e, ratio, gates, values, gamma, rope_dim, rope_base=10000.0, eps=1e-6):
+    y = csa.pool(gates, values)
+    y = csa.rope(y, e * ratio, rope_dim, rope_base)
+    return csa.rms_norm(y, gamma, eps)
+
+
+def _entry_rope_at_group_end(e, ratio, gates, values, gamma, rope_dim, rope_base=10000.0, eps=1e-6):
+    y = csa.rms_norm(csa.pool(gates, values), gamma, eps)
+    return csa.rope(y, (e + 1) * ratio - 1, rope_dim, rope_base)
+
+
+def _rms_eps_outside_root(y, gamma, eps):
+    y = np.asarray(y, float)
+    return y / (np.sqrt(np.mean(y * y, axis=-1, keepdims=True)) + eps) * gamma
 
 
 def _rms_no_sqrt(y, gamma, eps):
@@ -101,6 +117,9 @@ MUTATIONS = {
     "rope_wrong_sign": ("rope", _rope_sign),
     "rope_half_split_pairs": ("rope", _rope_half_split),
     "rmsnorm_without_sqrt": ("rms_norm", _rms_no_sqrt),
+    "rmsnorm_eps_outside_the_root": ("rms_norm", _rms_eps_outside_root),
+    "entry_rope_before_gain_scaled_norm": ("entry_from_rows", _entry_rope_before_norm),
+    "entry_rotated_at_its_last_token": ("entry_from_rows", _entry_rope_at_group_end),
     "indexer_without_relu": ("index_score", _index_no_relu),
     "indexer_head_weights_misindexed": ("index_score", _index_w_reversed),
     "topk_ties_to_higher_index": ("topk", _topk_ties_high),
@@ -115,6 +134,7 @@ PINS = [
     P.test_pooled_scalar_7_4_pool, P.test_minus_inf_candidates_are_never_read,
     P.test_equal_gates_give_the_arithmetic_mean, P.test_pool_matches_scalar_brute_force,
     P.test_rms_norm_unit_rms_and_scale_invariance, P.test_rope_matches_complex_rotation,
+    P.test_entry_pool_norm_gain_rope_order_hand_worked,
     P.test_rope_large_position_angle_in_float64,
     A.test_sink_closed_form, A.test_sink_limits_and_textbook_softmax,
     A.test_attention_matches_torch_sdpa_with_sink_column, A.test_index_score_brute_force_and_mask,

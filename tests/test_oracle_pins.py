@@ -46,6 +46,38 @@ def test_pooled_scalar_7_4_through_compress_entry():
     assert np.allclose(y, pre / np.sqrt(np.mean(pre ** 2)), rtol=0, atol=1e-12)
 
 
+def _entry_order_case():
+    g = read_golden("entry_order.txt")
+    D, r, e = int(g["D"][0]), int(g["ratio"][0]), int(g["entry"][0])
+    gates1 = _floats(g["gates"])
+    u, signs = _floats(g["u"]), _floats(g["signs"])
+    kv = u[:, None] * signs[None, :]                  # token j: (u_j, u_j, -u_j, u_j)
+    gate = np.repeat(gates1[:, None], D, axis=1)      # the same gates on every channel
+    return g, D, r, e, kv, gate
+
+
+def test_entry_pool_norm_gain_rope_order_hand_worked():
+    """Pooling, then RMSNorm with a non-uniform gain (eps inside the root),
+    then RoPE of the trailing pair at position e*r: a hand-worked entry whose
+    rotated pair has unequal gains, so rotating before the gain-scaled norm
+    (or at another position, or on the leading pair) gives other numbers."""
+    g, D, r, e, kv, gate = _entry_order_case()
+    gamma, eps = _floats(g["gamma"]), float(g["eps"][0])
+    rd, base = int(g["rope_dim"][0]), float(g["rope_base"][0])
+    want = _floats(g["expected"])
+    prev, cur = csa.entry_candidates(e, r, int(g["overlap"][0]))
+    assert prev == [0, 1] and cur == [2, 3]
+    got = csa.compress_entry(e, kv, gate, kv, gate, gamma, r, 1, rd, base, eps)
+    assert np.allclose(got, want, rtol=0, atol=1e-12)
+    got2 = csa.entry_from_rows(e, r, gate, kv, gamma, rd, base, eps)
+    assert np.allclose(got2, want, rtol=0, atol=1e-12)
+    # the streaming compressor emits the same entry when token 3 completes group 1
+    sc = csa.StreamingCompressor(gamma, r, 1, rd, base, eps)
+    emitted = [sc.push(t, kv[t], gate[t]) for t in range(4)]
+    assert emitted == [None, 0, None, 1]
+    assert np.allclose(sc.cache[1], want, rtol=0, atol=1e-12)
+
+
 def test_minus_inf_candidates_are_never_read():
     """A -inf gate excludes its value even when that value is NaN or inf."""
     gates = np.array([[-np.inf], [-np.inf], [0.0], [0.0]])
