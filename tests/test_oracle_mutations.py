@@ -8,8 +8,10 @@ import pytest
 
 import oracle
 from oracle import csa
+from oracle import projection
 from tests import test_oracle_attention as A
 from tests import test_oracle_pins as P
+from tests import test_oracle_projection as Q
 
 _orig = {name: getattr(csa, name) for name in ("pool", "rope", "rms_norm", "index_score", "topk", "attend",
                                                 "window_positions", "sparse_attn", "entry_from_rows")}
@@ -111,7 +113,59 @@ def _sparse_no_inverse_rope(q, cmp, sel, win_rows, sink, scale, pos, rope_dim, r
     return _orig["sparse_attn"](q, cmp, sel, win_rows, sink, scale, pos, 0, rope_base)
 
 
+_orig_proj = {name: getattr(projection, name) for name in ("q_path", "grouped_down", "out_proj")}
+
+
+def _q_no_latent_norm(x, wq_a, gamma_q, wq_b, heads, head_dim, pos, rope_dim, rope_base=10000.0, eps=1e-6):
+    x = np.asarray(x, float)
+    q = ((x @ np.asarray(wq_a, float).T) * gamma_q @ np.asarray(wq_b, float).T).reshape(*x.shape[:-1], heads, head_dim)
+    q = q / np.sqrt(np.mean(q * q, axis=-1, keepdims=True) + eps)
+    return csa.rope(q, np.broadcast_to(np.asarray(pos)[..., None], q.shape[:-1]), rope_dim, rope_base)
+
+
+def _q_norm_over_all_heads(x, wq_a, gamma_q, wq_b, heads, head_dim, pos, rope_dim, rope_base=10000.0, eps=1e-6):
+    x = np.asarray(x, float)
+    qr = csa.rms_norm(x @ np.asarray(wq_a, float).T, gamma_q, eps)
+    q = qr @ np.asarray(wq_b, float).T
+    q = (q / np.sqrt(np.mean(q * q, axis=-1, keepdims=True) + eps)).reshape(*x.shape[:-1], heads, head_dim)
+    return csa.rope(q, np.broadcast_to(np.asarray(pos)[..., None], q.shape[:-1]), rope_dim, rope_base)
+
+
+def _q_rope_on_leading_dims(x, wq_a, gamma_q, wq_b, heads, head_dim, pos, rope_dim, rope_base=10000.0, eps=1e-6):
+    q = _orig_proj["q_path"](x, wq_a, gamma_q, wq_b, heads, head_dim, np.zeros_like(np.asarray(pos)), rope_dim,
+                             rope_base, eps)
+    flipped = q[..., ::-1].copy()             # rotate the first rope_dim dims instead of the last
+    p = np.broadcast_to(np.asarray(pos)[..., None], q.shape[:-1])
+    return csa.rope(flipped, p, rope_dim, rope_base)[..., ::-1]
+
+
+def _grouped_interleaved_heads(o, wo_a, groups):
+    o = np.asarray(o, float)
+    H = o.shape[-2]
+    perm = np.argsort(np.arange(H) % groups, kind="stable")   # group g = heads g, g+G, g+2G, ...
+    return _orig_proj["grouped_down"](o[..., perm, :], wo_a, groups)
+
+
+def _grouped_transposed_weight(o, wo_a, groups):
+    o = np.asarray(o, float)
+    og = o.reshape(*o.shape[:-2], groups, -1)
+    w = np.asarray(wo_a, float)
+    return np.einsum("...gd,gdr->...gr", og, w.reshape(w.shape[0], w.shape[2], w.shape[1]))
+
+
+def _out_proj_without_up(o, wo_a, wo_b, groups):
+    r = projection.grouped_down(o, wo_a, groups)
+    y = r.reshape(*r.shape[:-2], -1)
+    return y[..., :np.asarray(wo_b).shape[0]]
+
+
 MUTATIONS = {
+    "q_path_latent_norm_dropped": ("q_path", _q_no_latent_norm),
+    "q_path_norm_over_all_heads": ("q_path", _q_norm_over_all_heads),
+    "q_path_rope_on_leading_dims": ("q_path", _q_rope_on_leading_dims),
+    "out_proj_groups_interleave_heads": ("grouped_down", _grouped_interleaved_heads),
+    "out_proj_down_weight_transposed": ("grouped_down", _grouped_transposed_weight),
+    "out_proj_up_projection_dropped": ("out_proj", _out_proj_without_up),
     "pool_softmax_over_channels": ("pool", _pool_wrong_axis),
     "pool_zero_padding_for_missing_group": ("pool", _pool_zero_instead_of_minus_inf),
     "rope_wrong_sign": ("rope", _rope_sign),
@@ -141,13 +195,17 @@ PINS = [
     A.test_topk_brute_force_and_minus_inf, A.test_full_topk_equals_dense_attention,
     A.test_inverse_rope_on_output_undoes_a_rotated_single_row, A.test_window_positions,
     lambda: A.test_topk_matches_stable_argsort(64, 64, 8),
+    Q.test_grouped_projection_is_a_block_diagonal_matmul, Q.test_each_group_reads_only_its_own_heads,
+    Q.test_q_path_matches_torch_rms_norm_and_complex_rotation,
+    Q.test_q_heads_have_unit_rms_and_rope_spares_the_leading_dims, Q.test_low_rank_query_is_a_two_step_product,
 ]
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_planted_mistake_is_caught(name, monkeypatch):
     attr, fn = MUTATIONS[name]
-    monkeypatch.setattr(csa, attr, fn)
+    mod = projection if attr in _orig_proj else csa
+    monkeypatch.setattr(mod, attr, fn)
     if hasattr(oracle, attr):
         monkeypatch.setattr(oracle, attr, fn)
     caught = 0
