@@ -7,9 +7,10 @@ step and a thin ctypes binding with the same function names.
 from ._lib import (CSA_BF16, CSA_F32, CsaError, csa_compress, csa_compress_jobs,  # noqa: F401
                    csa_compress_workspace_size,
                    csa_index_score,
-                   csa_sparse_attn, csa_sparse_attn_workspace_size, csa_topk, csa_topk_workspace_size,
+                   csa_sparse_attn, csa_sparse_attn_workspace_size, csa_topk, csa_topk_noalloc, csa_topk_workspace_size,
+                   CSA_TOPK_NOALLOC_SCRATCH_BYTES,
                    hca_attn, hca_attn_workspace_size, lib, LIB_PATH)
 
-__all__ = ["csa_compress", "csa_compress_jobs", "csa_compress_workspace_size", "csa_index_score", "csa_topk", "csa_topk_workspace_size", "csa_sparse_attn",
+__all__ = ["csa_compress", "csa_compress_jobs", "csa_compress_workspace_size", "csa_index_score", "csa_topk", "csa_topk_noalloc", "csa_topk_workspace_size", "csa_sparse_attn",
            "csa_sparse_attn_workspace_size", "hca_attn", "hca_attn_workspace_size", "CsaError", "lib",
-           "CSA_F32", "CSA_BF16", "LIB_PATH"]
+           "CSA_F32", "CSA_BF16", "CSA_TOPK_NOALLOC_SCRATCH_BYTES", "LIB_PATH"]

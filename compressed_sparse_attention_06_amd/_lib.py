@@ -47,6 +47,7 @@ SIGNATURES = {
                                  _c_p, _c_p]),
     "csa_topk_workspace_size": (_c_sz, [_c_int, _c_int, _c_int]),
     "csa_topk": (_c_int, [_c_p, _c_p, _c_int, _c_int, _c_int, _c_p, _c_p, _c_sz, _c_p]),
+    "csa_topk_noalloc": (_c_int, [_c_p, _c_p, _c_int, _c_int, _c_int, _c_p, _c_p]),
     "csa_sparse_attn_workspace_size": (_c_sz, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "csa_sparse_attn": (_c_int, [_c_p, _c_p, _c_int, _c_p, _c_int, _c_p, _c_int, _c_int, _c_p, _c_p, _c_int, _c_f,
                                  _c_int, _c_f, _c_int, _c_int, _c_int, _c_int, _c_p, _c_int, _c_p, _c_sz, _c_p]),
@@ -198,6 +199,18 @@ def csa_topk(scores, n_valid, k, idx, *, ws=None, stream=None):
     return idx
 
 
+CSA_TOPK_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def csa_topk_noalloc(scores, n_valid, k, idx, *, stream=None):
+    """csa_topk with the library's static scratch instead of a workspace (allocates nothing)."""
+    R, N = scores.shape
+    _dense(scores, n_valid, idx)
+    st = lib().csa_topk_noalloc(_ptr(scores), _ptr(n_valid), R, N, k, _ptr(idx), _stream(stream))
+    _check(st, "csa_topk_noalloc")
+    return idx
+
+
 def csa_sparse_attn_workspace_size(B, S, H, D, k, window):
     return int(lib().csa_sparse_attn_workspace_size(B, S, H, D, k, window))
 
@@ -232,3 +245,4 @@ def hca_attn(q, cmp, win, pos, sink, out, *, ratio, window, scale, rope_dim, rop
                         _bytes(ws), _stream(stream))
     _check(st, "hca_attn")
     return out
+

@@ -182,6 +182,17 @@ int csa_topk(const float* scores, const int* n_valid, int R, int N, int k, int* 
   return hip_status(csa::launch_topk(scores, n_valid, R, N, k, idx, ws, stream));
 }
 
+int csa_topk_noalloc(const float* scores, const int* n_valid, int R, int N, int k, int* idx, hipStream_t stream) {
+  if (!scores || !idx || R < 0 || N < 0 || k < 1 || k > 4096) return CSA_ERR_INVALID_ARG;
+  if (R > INT32_MAX / 2) return CSA_ERR_UNSUPPORTED;
+  if ((int64_t(N) + 16383) / 16384 > kMaxGridY) return CSA_ERR_UNSUPPORTED;
+  const csa::TopkPlan plan = csa::plan_topk(R, N, k);
+  if (plan.ws_bytes > CSA_TOPK_NOALLOC_SCRATCH_BYTES) return CSA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (plan.ws_bytes > 0 && csa::topk_scratch(&ws) != hipSuccess) return CSA_ERR_HIP;
+  return hip_status(csa::launch_topk(scores, n_valid, R, N, k, idx, ws, stream));
+}
+
 namespace {
 
 int attn_common(const void* q, const void* cmp, int Ncap, const int* idx, int k, int ratio, const void* win, int Wcap,
@@ -268,3 +279,4 @@ int hca_attn(const void* q, const void* cmp, int Ncap, int ratio, const void* wi
 }
 
 }  // extern "C"
+

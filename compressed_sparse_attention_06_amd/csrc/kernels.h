@@ -59,6 +59,9 @@ struct TopkPlan {
   size_t ws_bytes;
 };
 TopkPlan plan_topk(int R, int N, int k);
+// Device address of the current device's top-k scratch array
+// (CSA_TOPK_NOALLOC_SCRATCH_BYTES), looked up on first use per device.
+hipError_t topk_scratch(void** out);
 hipError_t launch_topk(const float* scores, const int* n_valid, int R, int N, int k, int* idx,
                        void* ws, hipStream_t stream);
 

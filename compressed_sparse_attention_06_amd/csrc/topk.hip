@@ -22,9 +22,17 @@
 // top-k under the same (key desc, index asc) order.  Candidate lists are
 // reduced again until one tile remains.
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "kernels.h"
+
+// Scratch of the no-allocation top-k (csa_topk_noalloc): the two chunk
+// candidate buffers of rows longer than one tile, for callers that cannot
+// allocate.  Every device the library runs on holds its own copy until the
+// process ends.  In host code this name is only a stand-in for the device
+// array: host code uses the address that topk_scratch() looks up.
+static __device__ __align__(256) unsigned char scratch[CSA_TOPK_NOALLOC_SCRATCH_BYTES];
 
 namespace csa {
 namespace {
@@ -420,6 +428,27 @@ TopkPlan plan_topk(int R, int N, int k) {
   TopkPlan p{L.n - 1, int64_t(R) * L.cand_max, 0};
   p.ws_bytes = p.levels ? size_t(2) * size_t(p.cand_elems) * (sizeof(uint32_t) + sizeof(int)) : 0;
   return p;
+}
+
+// Device address of this device's scratch array, looked up once per device
+// (with that device current) and kept.
+hipError_t topk_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_topk(const float* scores, const int* n_valid, int R, int N, int k, int* idx, void* ws,

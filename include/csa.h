@@ -207,6 +207,27 @@ int csa_topk(const float* scores, const int* n_valid, int R, int N, int k, int* 
              void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * csa_topk_noalloc -- csa_topk without a caller workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).
+ *
+ * Same arguments, results and validation as csa_topk, bit for bit.  Rows of
+ * at most 16,384 positions need no scratch; longer rows keep their chunk
+ * candidates in a static device array of CSA_TOPK_NOALLOC_SCRATCH_BYTES
+ * (16 MiB) that every device the library runs on holds until the process
+ * ends (its address is looked up on the first call on each device).  Calls
+ * needing more than that (csa_topk_workspace_size(R, N, k) above the limit,
+ * e.g. 32 rows of 262,144 positions at k = 1024 fit, 64 such rows do not)
+ * return CSA_ERR_WORKSPACE.  The call allocates and frees nothing.  All calls
+ * on one device share the one array: calls that may overlap in time on one
+ * device (different streams without ordering between them) race and must
+ * not be issued.  Nothing in the array needs to start at zero.
+ */
+#define CSA_TOPK_NOALLOC_SCRATCH_BYTES (16u << 20)
+int csa_topk_noalloc(const float* scores, const int* n_valid, int R, int N, int k, int* idx,
+                     hipStream_t stream);
+
+/*
  * csa_sparse_attn -- CSA joint-softmax attention with a sink.
  *
  * [V4-Flash walkthrough] "局部和压缩记忆，共用一次归一化": the window rows and

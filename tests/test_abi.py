@@ -164,6 +164,22 @@ def test_topk_validation_and_workspace(lib):
     assert lib.csa_topk(P, None, 32, 262144, 512, P, None, need, None) == WORKSPACE
 
 
+def test_topk_noalloc_validation(lib):
+    """The no-allocation top-k validates like csa_topk and rejects calls whose
+    chunk candidates exceed its 16 MiB static scratch (checked before any HIP
+    call)."""
+    from compressed_sparse_attention_06_amd import CSA_TOPK_NOALLOC_SCRATCH_BYTES
+    assert CSA_TOPK_NOALLOC_SCRATCH_BYTES == 16 << 20
+    assert lib.csa_topk_noalloc(None, None, 1, 10, 4, P, None) == INVALID
+    assert lib.csa_topk_noalloc(P, None, 1, 10, 0, P, None) == INVALID
+    assert lib.csa_topk_noalloc(P, None, 1, 10, 4097, P, None) == INVALID
+    assert lib.csa_topk_noalloc(P, None, 1, 10, 4, None, None) == INVALID
+    # 32 rows of 262,144 at k = 1024 need exactly the scratch; 64 such rows need twice it
+    assert lib.csa_topk_workspace_size(32, 262144, 1024) == 16 << 20
+    assert lib.csa_topk_noalloc(P, None, 64, 262144, 1024, P, None) == WORKSPACE
+    assert lib.csa_topk_noalloc(P, None, 33, 262144, 1024, P, None) == WORKSPACE
+
+
 def _attn(lib, **kw):
     a = dict(q=P, cmp=P, Ncap=1000, idx=P, k=512, win=P, Wcap=128, window=128, pos=P, sink=P, dtype=1, scale=0.04,
              rope_dim=64, rope_base=10000.0, B=8, S=1, H=64, D=512, out=P, out_dtype=0, ws=P, ws_bytes=1 << 40,
