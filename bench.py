@@ -45,7 +45,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="csa_decode_64k", choices=sorted(synth.CONFIGS))
-    ap.add_argument("--extra", default="hca_decode_1m,csa_decode_1m,csa_prefill_8k,csa_decode_64k_k1024",
+    ap.add_argument("--extra", default="hca_decode_1m,csa_decode_1m,csa_prefill_8k,csa_decode_64k_k1024,"
+                    "attn_block_decode_64k",
                     help="comma-separated secondary workloads measured after the main one ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -241,6 +242,79 @@ class DecodeWorkload:
         return d
 
 
+class BlockWorkload(DecodeWorkload):
+    """One whole attention block at decode: the low-rank query path
+    (csa_q_proj) makes the queries the CSA step attends with, the CSA decode
+    step runs as in DecodeWorkload (its attention output in bf16), and the
+    grouped output projection (csa_out_proj) maps it back to the model width.
+    The 200 MiB of projection weights rotate over 4 copies, so the Infinity
+    Cache cannot serve them either."""
+
+    WEIGHT_COPIES = 4
+
+    def __init__(self, cfg, device, copies=COPIES, batch=None):
+        import torch
+        import compressed_sparse_attention_06_amd as csa
+        super().__init__(cfg, device, copies=copies, batch=batch)
+        dims = synth.FLASH_PROJ
+        self.dims = dims
+        B, H, D = self.cfg.B, self.cfg.H, self.cfg.D
+        wts = synth.proj_weights(self.cfg.cid, H, D, dims)
+        self.gamma_q = _f32(wts["gamma_q"], device)
+        self.wcopies = self.WEIGHT_COPIES
+        self.wts = {}
+        for name in ("wq_a", "wq_b", "wo_a", "wo_b"):
+            w0 = _bf16(wts[name], device)
+            self.wts[name] = [w0] + [w0.clone() for _ in range(self.wcopies - 1)]
+        self.x = _bf16(synth.hidden_states(self.cfg.cid, B, dims.d_model), device)
+        self.q = torch.empty((B, 1, H, D), dtype=torch.bfloat16, device=device)   # made by the query path
+        self.out = torch.empty((B, 1, H, D), dtype=torch.bfloat16, device=device)  # attention output
+        self.y = torch.empty((B, dims.d_model), dtype=torch.float32, device=device)
+        self.ws_q = torch.empty(csa.csa_q_proj_workspace_size(B, dims.d_model, dims.q_rank, H, D), dtype=torch.uint8,
+                                device=device)
+        self.ws_o = torch.empty(csa.csa_out_proj_workspace_size(B, H, D, dims.groups, dims.o_rank, dims.d_model),
+                                dtype=torch.uint8,
+                                device=device)
+        self.pos_flat = self.pos.view(B)
+        torch.cuda.synchronize()
+
+    def launches(self, c):
+        import compressed_sparse_attention_06_amd as csa
+        cfg, w = self.cfg, self.wts
+        cw = c % self.wcopies
+        L = [("q_proj", lambda: csa.csa_q_proj(self.x, w["wq_a"][cw], self.gamma_q, w["wq_b"][cw], self.pos_flat,
+                                               self.q.view(cfg.B, cfg.H, cfg.D), rope_dim=cfg.rope_dim,
+                                               rope_base=cfg.rope_base, eps=cfg.eps, ws=self.ws_q))]
+        L += super().launches(c)
+        L.append(("out_proj", lambda: csa.csa_out_proj(self.out.view(cfg.B, cfg.H, cfg.D), w["wo_a"][cw],
+                                                       w["wo_b"][cw], self.y, ws=self.ws_o)))
+        return L
+
+    def dominant(self):
+        return "out_proj"
+
+    def algorithmic(self):
+        by, fl = super().algorithmic()
+        cfg, d, B = self.cfg, self.dims, self.cfg.B
+        HD = cfg.H * cfg.D
+        by["sparse_attn"] -= B * HD * 2      # the attention output is bf16 here
+        by["q_proj"] = 2 * (d.q_rank * d.d_model + HD * d.q_rank) + B * d.d_model * 2 + B * 4 + d.q_rank * 4 + B * HD * 2
+        by["out_proj"] = 2 * (d.groups * d.o_rank * (HD // d.groups) + d.d_model * d.groups * d.o_rank) + \
+            B * HD * 2 + B * d.d_model * 4
+        fl["q_proj"] = 2 * B * (d.q_rank * d.d_model + HD * d.q_rank)
+        fl["out_proj"] = 2 * B * (d.o_rank * HD + d.d_model * d.groups * d.o_rank)
+        return by, fl
+
+    def unit(self):
+        return "per projection weight: 2 B read (8 tokens: 16 flop)"
+
+    def describe(self):
+        d = super().describe()
+        d.update(d_model=self.dims.d_model, q_rank=self.dims.q_rank, out_groups=self.dims.groups,
+                 out_rank=self.dims.o_rank, weight_copies=self.wcopies)
+        return d
+
+
 class PrefillWorkload:
     """CSA prefill of S tokens: compress all groups, score, top-k, attention."""
 
@@ -321,11 +395,16 @@ class PrefillWorkload:
         vis = (t + 1) // r
         win = np.minimum(cfg.window, t + 1)
         sel = np.minimum(vis, cfg.k)
+        # compulsory HBM bytes: every input read once, every output written
+        # once; the attention's gathers of selected rows (each query re-reads
+        # up to 640 rows of a 2 MiB cache, ~4.8 GB in all) are served from L2
+        # and the Infinity Cache and are reported apart (gathered_bytes)
         by = {"compress_kv": S * D * 2 * 2 + self.Nc * D * 2, "compress_idx": S * DI * 2 * 2 + self.Nc * DI * 2,
               "index_score": S * HI * DI * 2 + S * HI * 4 + self.Nc * DI * 2 + S * self.Nc * 4,
               "topk": S * self.Nc * 4 + S * cfg.k * 4,
-              "sparse_attn": int(S * H * D * 2 * 2 + np.sum(sel + win) * D * 2 + S * cfg.k * 4)}
+              "sparse_attn": int(S * H * D * 2 * 2 + self.Nc * D * 2 + S * D * 2 + S * cfg.k * 4)}
         fl = {"index_score": int(np.sum(vis)) * HI * DI * 2, "sparse_attn": int(np.sum(sel + win)) * H * D * 4}
+        self.gathered_bytes = int(np.sum(sel + win) * D * 2)
         return by, fl
 
     def unit(self):
@@ -342,6 +421,8 @@ def make_workload(name, device):
     cfg = synth.CONFIGS[name]
     if cfg.kind == "decode":
         return DecodeWorkload(cfg, device)
+    if cfg.kind == "block":
+        return BlockWorkload(cfg, device)
     if cfg.kind == "prefill":
         return PrefillWorkload(cfg, device)
     raise SystemExit(f"{name} is a parity-test configuration, not a bench workload")
@@ -486,24 +567,41 @@ def cpu_baseline_decode(wl, seconds):
             d["kv"][e] = oracle.entry_from_rows(e, cfg.ratio, rows(s.gate_stage), rows(s.kv_stage), shared["gamma"],
                                                 cfg.rope_dim, cfg.rope_base, cfg.eps)
         win = np.stack([f64(s.win[p % cfg.window]) for p in oracle.window_positions(s.pos, cfg.window)])
-        q = f64(s.q)
+        q = d["q_override"] if "q_override" in d else f64(s.q)
         if cfg.csa:
             if emit:
                 d["idx"][e] = oracle.entry_from_rows(e, cfg.ratio, rows(s.gi_stage), rows(s.ki_stage),
                                                      shared["gamma_idx"], cfg.rope_dim_idx, cfg.rope_base, cfg.eps)
-            pipeline.csa_query(q, f64(s.q_idx), s.w, d["kv"], d["idx"], s.n_vis, win, shared["sink"], cfg.k,
-                               scale, s.pos, cfg.rope_dim, cfg.rope_base)
-        else:
-            oracle.hca_attn(q, d["kv"], s.n_vis, win, shared["sink"], scale, s.pos, cfg.rope_dim, cfg.rope_base)
+            return pipeline.csa_query(q, f64(s.q_idx), s.w, d["kv"], d["idx"], s.n_vis, win, shared["sink"],
+                                      cfg.k, scale, s.pos, cfg.rope_dim, cfg.rope_base)[2]
+        return oracle.hca_attn(q, d["kv"], s.n_vis, win, shared["sink"], scale, s.pos, cfg.rope_dim, cfg.rope_base)
+
+    block = isinstance(wl, BlockWorkload)
+    if block:
+        from oracle import projection
+        wts = synth.proj_weights(cfg.cid, cfg.H, cfg.D, wl.dims)
+        wf = {k: (f64(v) if v.dtype == np.uint16 else v) for k, v in wts.items()}
+        xs = f64(synth.hidden_states(cfg.cid, cfg.B, wl.dims.d_model))
+        inner = one
+
+        def one(d):  # noqa: F811 -- the block: query path, the CSA step, output projection
+            s = d["seq"]
+            q = projection.q_path(xs[s.b], wf["wq_a"], wf["gamma_q"], wf["wq_b"], cfg.H, cfg.D, s.pos,
+                                  cfg.rope_dim, cfg.rope_base, cfg.eps)
+            d["q_override"] = q
+            o = inner(d)
+            projection.out_proj(o, wf["wo_a"], wf["wo_b"], wl.dims.groups)
 
     n, t0 = 0, time.perf_counter()
     while time.perf_counter() - t0 < seconds:
         one(prepared[n % len(prepared)])
         n += 1
     dt = time.perf_counter() - t0
+    what = ("query path, compress the completed group, score, top-k, attend, output projection" if block else
+            "compress the completed group, score, top-k, attend")
     return dict(value=n / dt, unit="query-tokens/s", cores=cpu_threads(), kind="oracle",
                 sample=f"{n} decode queries of {cfg.name} (sequences 0..{len(prepared) - 1} in turn, float64 "
-                       f"NumPy oracle: compress the completed group, score, top-k, attend), {dt:.1f} s")
+                       f"NumPy oracle: {what}), {dt:.1f} s")
 
 
 def cpu_baseline_prefill(wl, seconds):
@@ -532,6 +630,12 @@ def cpu_baseline_prefill(wl, seconds):
                        f"(score 2048 entries, top-k, attend), float64 NumPy oracle, {dt:.1f} s")
 
 
+def cpu_baseline(wl, seconds):
+    if isinstance(wl, PrefillWorkload):
+        return cpu_baseline_prefill(wl, seconds)
+    return cpu_baseline_decode(wl, seconds)
+
+
 # ---------------------------------------------------------------------------
 def measure(wl, steps, warmup, only=None):
     per, total = time_steps(wl, steps, warmup, only)
@@ -545,7 +649,8 @@ def measure(wl, steps, warmup, only=None):
     return res
 
 
-KERNEL_SOURCE = {"index_score": "index_score.hip", "topk": "topk.hip", "sparse_attn": "attn.hip",
+KERNEL_SOURCE = {"q_proj": "proj.hip", "out_proj": "proj.hip",
+                 "index_score": "index_score.hip", "topk": "topk.hip", "sparse_attn": "attn.hip",
                  "hca_attn": "attn.hip", "compress": "compress.hip", "compress_kv": "compress.hip",
                  "compress_idx": "compress.hip"}
 
@@ -555,23 +660,34 @@ def measured_traffic(workload, kernel):
     summary of this workload (profiles/*_<workload>.md: FETCH_SIZE and
     WRITE_SIZE scaled by a plain copy), or None when there is none or the
     kernel source has changed since the counters were taken."""
-    import glob
+    v = _profile_field(workload, kernel, "traffic_bytes_per_launch")
+    return None if v is None else int(v)
+
+
+def _source_hash(kernel):
     import hashlib
     csrc = os.path.join(ROOT, "compressed_sparse_attention_06_amd", "csrc")
     h = hashlib.sha256()
     for f in (KERNEL_SOURCE[kernel], "common.h", "kernels.h", "rope_math.h"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
+    return h.hexdigest()
+
+
+def _profile_field(workload, kernel, key):
+    """A numeric field of the committed profile summary of `workload` whose
+    traffic_kernel is `kernel`, if its source hash matches the current source."""
+    import glob
+    want = _source_hash(kernel)
     for path in glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}.md")):
         fields = {}
         with open(path) as fh:
             for line in fh:
-                if ":" in line and line.split(":", 1)[0] in ("traffic_kernel", "traffic_bytes_per_launch",
-                                                              "source_sha256"):
+                if ":" in line and line.split(":", 1)[0] in ("traffic_kernel", key, "source_sha256"):
                     k, v = line.split(":", 1)
                     fields[k] = v.strip()
-        if fields.get("traffic_kernel") == kernel and fields.get("source_sha256") == h.hexdigest():
-            return int(float(fields["traffic_bytes_per_launch"]))
+        if fields.get("traffic_kernel") == kernel and fields.get("source_sha256") == want and key in fields:
+            return float(fields[key])
     return None
 
 
@@ -588,10 +704,24 @@ def roofline(wl, m):
                 per_unit=wl.unit())
 
 
+def measured_mfma_util(workload, kernel):
+    """Matrix-core busy fraction of `kernel` from the committed rocprofv3
+    counter summary (SQ_VALU_MFMA_BUSY_CYCLES over SIMD cycles), or None when
+    there is none or the kernel source changed since it was taken."""
+    return _profile_field(workload, kernel, "mfma_busy_frac")
+
+
 def summary(wl, m):
     q = wl.queries()
     per = m["per"] * 1e3
-    return dict(query_tokens_per_s=round(q / (m["ms_per_step"] * 1e-3), 1), ms_per_step=round(m["ms_per_step"], 5),
+    extra = {}
+    if isinstance(wl, PrefillWorkload):
+        t_attn = m["kern"]["sparse_attn"] * 1e-6
+        extra = dict(indexer_mfma_util=round(m["fl"]["index_score"] / (m["dom_ms"] * 1e-3) / 1e12 /
+                                             MFMA_BF16_PEAK_TFLOPS, 4),
+                     indexer_mfma_busy_counters=measured_mfma_util(wl.cfg.name, "index_score"),
+                     attn_gathered_rows_gbs=round(wl.gathered_bytes / t_attn / 1e9, 1))
+    return dict(**extra,query_tokens_per_s=round(q / (m["ms_per_step"] * 1e-3), 1), ms_per_step=round(m["ms_per_step"], 5),
                 step_us_p50=round(float(np.percentile(per, 50)), 2), step_us_p95=round(float(np.percentile(per, 95)), 2),
                 step_us_p99=round(float(np.percentile(per, 99)), 2),
                 hbm_gbs_step=round(m["step_bytes"] / (m["ms_per_step"] * 1e-3) / 1e9, 1),
@@ -635,10 +765,7 @@ def main():
         line[key] = main_sum[key]
     line["setup_s"] = round(setup_s, 1)
     if not args.no_cpu_baseline:
-        if isinstance(wl, PrefillWorkload):
-            line["cpu_baseline"] = cpu_baseline_prefill(wl, args.cpu_seconds)
-        else:
-            line["cpu_baseline"] = cpu_baseline_decode(wl, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
         note(f"cpu baseline: {line['cpu_baseline']['value']:.2f} {line['cpu_baseline']['unit']}")
     del wl
     torch.cuda.empty_cache()
@@ -649,8 +776,9 @@ def main():
         m2 = measure(w2, args.steps, args.warmup)
         note(f"{name}: {m2['ms_per_step'] * 1e3:.2f} us/step")
         extras[name] = summary(w2, m2)
-        if isinstance(w2, PrefillWorkload):
-            extras[name]["indexer_mfma_util"] = extras[name]["roofline"]["frac"]
+        if not args.no_cpu_baseline:
+            extras[name]["cpu_baseline"] = cpu_baseline(w2, args.cpu_seconds / 2)
+            note(f"{name} cpu baseline: {extras[name]['cpu_baseline']['value']:.2f} query-tokens/s")
         del w2
         torch.cuda.empty_cache()
     if extras:

@@ -9,8 +9,10 @@ from ._lib import (CSA_BF16, CSA_F32, CsaError, csa_compress, csa_compress_jobs,
                    csa_index_score,
                    csa_sparse_attn, csa_sparse_attn_workspace_size, csa_topk, csa_topk_noalloc, csa_topk_workspace_size,
                    CSA_TOPK_NOALLOC_SCRATCH_BYTES,
+                   csa_q_proj, csa_q_proj_workspace_size, csa_out_proj, csa_out_proj_workspace_size,
                    hca_attn, hca_attn_workspace_size, lib, LIB_PATH)
 
 __all__ = ["csa_compress", "csa_compress_jobs", "csa_compress_workspace_size", "csa_index_score", "csa_topk", "csa_topk_noalloc", "csa_topk_workspace_size", "csa_sparse_attn",
-           "csa_sparse_attn_workspace_size", "hca_attn", "hca_attn_workspace_size", "CsaError", "lib",
+           "csa_sparse_attn_workspace_size", "hca_attn", "hca_attn_workspace_size", "csa_q_proj",
+           "csa_q_proj_workspace_size", "csa_out_proj", "csa_out_proj_workspace_size", "CsaError", "lib",
            "CSA_F32", "CSA_BF16", "CSA_TOPK_NOALLOC_SCRATCH_BYTES", "LIB_PATH"]

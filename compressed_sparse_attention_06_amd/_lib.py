@@ -51,6 +51,12 @@ SIGNATURES = {
     "csa_sparse_attn_workspace_size": (_c_sz, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "csa_sparse_attn": (_c_int, [_c_p, _c_p, _c_int, _c_p, _c_int, _c_p, _c_int, _c_int, _c_p, _c_p, _c_int, _c_f,
                                  _c_int, _c_f, _c_int, _c_int, _c_int, _c_int, _c_p, _c_int, _c_p, _c_sz, _c_p]),
+    "csa_q_proj_workspace_size": (_c_sz, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "csa_q_proj": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_f, _c_f,
+                            _c_p, _c_p, _c_sz, _c_p]),
+    "csa_out_proj_workspace_size": (_c_sz, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
+    "csa_out_proj": (_c_int, [_c_p, _c_int, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_p, _c_int,
+                              _c_p, _c_sz, _c_p]),
     "hca_attn_workspace_size": (_c_sz, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "hca_attn": (_c_int, [_c_p, _c_p, _c_int, _c_int, _c_p, _c_int, _c_int, _c_p, _c_p, _c_int, _c_f, _c_int, _c_f,
                           _c_int, _c_int, _c_int, _c_int, _c_p, _c_int, _c_p, _c_sz, _c_p]),
@@ -246,3 +252,40 @@ def hca_attn(q, cmp, win, pos, sink, out, *, ratio, window, scale, rope_dim, rop
     _check(st, "hca_attn")
     return out
 
+
+def csa_q_proj_workspace_size(M, d_model, q_rank, H, head_dim):
+    return int(lib().csa_q_proj_workspace_size(M, d_model, q_rank, H, head_dim))
+
+
+def csa_q_proj(x, wq_a, gamma_q, wq_b, pos, q, *, rope_dim, rope_base=10000.0, eps=1e-6, ws=None, stream=None):
+    """x [M, d_model] bf16, wq_a [q_rank, d_model], gamma_q [q_rank] f32, wq_b [H*head_dim, q_rank], pos [M] i32
+    -> q [M, H, head_dim] bf16 (token rows may carry leading batch axes: x [..., d], q [..., H, head_dim])."""
+    d = x.shape[-1]
+    M = x.numel() // d
+    H, hd = q.shape[-2], q.shape[-1]
+    r = wq_a.shape[0]
+    _dense(x, wq_a, gamma_q, wq_b, pos, q)
+    ws = _ws(csa_q_proj_workspace_size(M, d, r, H, hd), ws, x.device)
+    st = lib().csa_q_proj(_ptr(x), _ptr(wq_a), _ptr(gamma_q), _ptr(wq_b), _ptr(pos), M, d, r, H, hd, rope_dim,
+                          rope_base, eps, _ptr(q), _ptr(ws), _bytes(ws), _stream(stream))
+    _check(st, "csa_q_proj")
+    return q
+
+
+def csa_out_proj_workspace_size(M, H, head_dim, groups, o_rank, d_model, o_dtype=CSA_BF16):
+    return int(lib().csa_out_proj_workspace_size(M, H, head_dim, groups, o_rank, d_model, o_dtype))
+
+
+def csa_out_proj(o, wo_a, wo_b, y, *, ws=None, stream=None):
+    """o [..., H, head_dim] (bf16 or f32), wo_a [groups, o_rank, H*head_dim/groups], wo_b [d_model, groups*o_rank]
+    -> y [..., d_model]."""
+    H, hd = o.shape[-2], o.shape[-1]
+    M = o.numel() // (H * hd)
+    groups, o_rank = wo_a.shape[0], wo_a.shape[1]
+    d = wo_b.shape[0]
+    _dense(o, wo_a, wo_b, y)
+    ws = _ws(csa_out_proj_workspace_size(M, H, hd, groups, o_rank, d, _dtype(o)), ws, o.device)
+    st = lib().csa_out_proj(_ptr(o), _dtype(o), _ptr(wo_a), _ptr(wo_b), M, H, hd, groups, o_rank, d, _ptr(y),
+                            _dtype(y), _ptr(ws), _bytes(ws), _stream(stream))
+    _check(st, "csa_out_proj")
+    return y

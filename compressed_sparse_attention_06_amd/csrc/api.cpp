@@ -280,3 +280,138 @@ int hca_attn(const void* q, const void* cmp, int Ncap, int ratio, const void* wi
 
 }  // extern "C"
 
+// ---------------------------------------------------------------------------
+// Projections on either side of the attention
+// ---------------------------------------------------------------------------
+namespace {
+
+bool proj_dims_ok(int M, int N, int K) { return M >= 0 && N > 0 && K > 0 && N % 16 == 0 && K % 128 == 0; }
+
+}  // namespace
+
+namespace {
+
+// fp32 workspace layout of the query path: latent partials, normalised
+// latent, head partials (floats)
+struct QPlan {
+  csa::ProjPlan p1, p2;
+  size_t part1, qrn, qf;
+};
+QPlan q_plan(int M, int d_model, int q_rank, int64_t hq) {
+  QPlan q;
+  q.p1 = csa::plan_proj(M, q_rank, d_model, 1, false);
+  q.p2 = csa::plan_proj(M, int(hq), q_rank, 1, true);
+  q.part1 = size_t(q.p1.ks) * M * q_rank;
+  q.qrn = size_t(M) * q_rank;
+  q.qf = size_t(q.p2.ks) * M * hq;
+  return q;
+}
+
+struct OPlan {
+  csa::ProjPlan pa, pb;
+  size_t r, y;
+};
+OPlan o_plan(int M, int groups, int o_rank, int64_t kg, int d_model, bool o_f32) {
+  OPlan o;
+  o.pa = csa::plan_proj(M, o_rank, int(kg), groups, o_f32);
+  o.pb = csa::plan_proj(M, d_model, groups * o_rank, 1, true);
+  o.r = size_t(o.pa.ks) * M * groups * o_rank;
+  o.y = o.pb.ks > 1 ? size_t(o.pb.ks) * M * d_model : 0;
+  return o;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t csa_q_proj_workspace_size(int M, int d_model, int q_rank, int H, int head_dim) {
+  if (M < 0 || d_model < 1 || q_rank < 1 || H < 1 || head_dim < 1) return 0;
+  if (d_model % 128 != 0 || q_rank % 128 != 0 || (int64_t(H) * head_dim) % 16 != 0) return 0;
+  const QPlan q = q_plan(M, d_model, q_rank, int64_t(H) * head_dim);
+  return (q.part1 + q.qrn + q.qf) * sizeof(float);
+}
+
+int csa_q_proj(const void* x, const void* wq_a, const float* gamma_q, const void* wq_b, const int* pos, int M,
+               int d_model, int q_rank, int H, int head_dim, int rope_dim, float rope_base, float eps, void* q,
+               void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!x || !wq_a || !gamma_q || !wq_b || !q || (M > 0 && rope_dim > 0 && !pos)) return CSA_ERR_INVALID_ARG;
+  if (M < 0 || d_model < 1 || q_rank < 1 || H < 1 || head_dim < 2) return CSA_ERR_INVALID_ARG;
+  if (rope_dim < 0 || rope_dim % 2 != 0 || rope_dim > head_dim) return CSA_ERR_INVALID_ARG;
+  if (!(eps >= 0.f) || !std::isfinite(eps) || !(rope_base > 0.f) || !std::isfinite(rope_base))
+    return CSA_ERR_INVALID_ARG;
+  const int64_t hq = int64_t(H) * head_dim;
+  if (hq > INT32_MAX / 2 || int64_t(M) * hq > (int64_t(1) << 40)) return CSA_ERR_UNSUPPORTED;
+  if (!proj_dims_ok(M, q_rank, d_model) || !proj_dims_ok(M, int(hq), q_rank) || q_rank > 16384 ||
+      head_dim > 16384)
+    return CSA_ERR_UNSUPPORTED;
+  if (int64_t(M) > 65535 * 32) return CSA_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(wq_a) || !aligned16(wq_b) || !aligned16(q)) return CSA_ERR_INVALID_ARG;
+  const size_t need = csa_q_proj_workspace_size(M, d_model, q_rank, H, head_dim);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return CSA_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(ws)) return CSA_ERR_INVALID_ARG;
+  if (M == 0) return CSA_OK;
+  const QPlan pl = q_plan(M, d_model, q_rank, hq);
+  float* part1 = static_cast<float*>(ws);
+  float* qrn = part1 + pl.part1;
+  float* qf = qrn + pl.qrn;
+  const double l2b = std::log2(double(rope_base));
+  // down-projection to the latent (K-chunk partials)
+  csa::ProjArgs g1{x,  CSA_BF16, d_model, 0, wq_a, 0, part1, CSA_F32, q_rank, 0, M, q_rank, d_model, 1, 1, 0,
+                   pl.p1.kc, pl.p1.ks, part1, int64_t(M) * q_rank};
+  if (csa::launch_proj_gemm(g1, stream) != hipSuccess) return CSA_ERR_HIP;
+  // RMSNorm of the latent (summing the partials), with its gain
+  csa::NormArgs n1{part1, q_rank, pl.p1.ks, int64_t(M) * q_rank, gamma_q, nullptr, qrn, CSA_F32, q_rank,
+                   M,     q_rank, 0,        l2b,                 eps};
+  if (csa::launch_rows_norm(n1, 1, stream) != hipSuccess) return CSA_ERR_HIP;
+  // up-projection to the heads
+  csa::ProjArgs g2{qrn, CSA_F32, q_rank, 0, wq_b, 0, qf, CSA_F32, hq, 0, M, int(hq), q_rank, 1, 1, 0,
+                   pl.p2.kc, pl.p2.ks, qf, int64_t(M) * hq};
+  if (csa::launch_proj_gemm(g2, stream) != hipSuccess) return CSA_ERR_HIP;
+  // per-head RMS (no gain), RoPE on each head's trailing dims, bf16 queries
+  csa::NormArgs n2{qf, hq, pl.p2.ks, int64_t(M) * hq, nullptr, pos, q, CSA_BF16, hq, M, head_dim, rope_dim, l2b,
+                   eps};
+  if (csa::launch_rows_norm(n2, H, stream) != hipSuccess) return CSA_ERR_HIP;
+  return CSA_OK;
+}
+
+size_t csa_out_proj_workspace_size(int M, int H, int head_dim, int groups, int o_rank, int d_model, int o_dtype) {
+  if (M < 0 || H < 1 || head_dim < 1 || groups < 1 || o_rank < 1 || d_model < 1) return 0;
+  const int64_t hd = int64_t(H) * head_dim;
+  if (hd % groups != 0 || (hd / groups) % 128 != 0 || (int64_t(groups) * o_rank) % 128 != 0) return 0;
+  const OPlan o = o_plan(M, groups, o_rank, hd / groups, d_model, o_dtype == CSA_F32);
+  return (o.r + o.y) * sizeof(float);
+}
+
+int csa_out_proj(const void* o, int o_dtype, const void* wo_a, const void* wo_b, int M, int H, int head_dim,
+                 int groups, int o_rank, int d_model, void* y, int y_dtype, void* ws, size_t ws_bytes,
+                 hipStream_t stream) {
+  if (!o || !wo_a || !wo_b || !y) return CSA_ERR_INVALID_ARG;
+  if (!dtype_ok(o_dtype) || !dtype_ok(y_dtype)) return CSA_ERR_INVALID_ARG;
+  if (M < 0 || H < 1 || head_dim < 1 || groups < 1 || o_rank < 1 || d_model < 1) return CSA_ERR_INVALID_ARG;
+  const int64_t hd = int64_t(H) * head_dim;
+  if (hd % groups != 0) return CSA_ERR_INVALID_ARG;
+  const int64_t kg = hd / groups, kb = int64_t(groups) * o_rank;
+  if (kg > INT32_MAX || kb > INT32_MAX) return CSA_ERR_UNSUPPORTED;
+  if (!proj_dims_ok(M, o_rank, int(kg)) || !proj_dims_ok(M, d_model, int(kb))) return CSA_ERR_UNSUPPORTED;
+  if (int64_t((o_rank + 127) / 128) * groups > 0x7fffffff || int64_t(M) > 65535 * 32) return CSA_ERR_UNSUPPORTED;
+  if (!aligned16(o) || !aligned16(wo_a) || !aligned16(wo_b) || !aligned16(y)) return CSA_ERR_INVALID_ARG;
+  const size_t need = csa_out_proj_workspace_size(M, H, head_dim, groups, o_rank, d_model, o_dtype);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return CSA_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(ws)) return CSA_ERR_INVALID_ARG;
+  if (M == 0) return CSA_OK;
+  const OPlan pl = o_plan(M, groups, o_rank, kg, d_model, o_dtype == CSA_F32);
+  float* r = static_cast<float*>(ws);
+  float* yp = r + pl.r;
+  // one down-projection per group of heads (K-chunk partials)
+  csa::ProjArgs ga{o, o_dtype, hd, kg, wo_a, int64_t(o_rank) * kg, r, CSA_F32, kb, o_rank, M, o_rank, int(kg),
+                   groups, 1, 0, pl.pa.kc, pl.pa.ks, r, int64_t(M) * kb};
+  if (csa::launch_proj_gemm(ga, stream) != hipSuccess) return CSA_ERR_HIP;
+  // the concatenated group results (summing the partials) back to the model width
+  csa::ProjArgs gb{r, CSA_F32, kb, 0, wo_b, 0, y, y_dtype, d_model, 0, M, d_model, int(kb), 1, pl.pa.ks,
+                   int64_t(M) * kb, pl.pb.kc, pl.pb.ks, yp, int64_t(M) * d_model};
+  if (csa::launch_proj_gemm(gb, stream) != hipSuccess) return CSA_ERR_HIP;
+  if (pl.pb.ks > 1 && csa::launch_proj_reduce(gb, stream) != hipSuccess) return CSA_ERR_HIP;
+  return CSA_OK;
+}
+
+}  // extern "C"

@@ -96,4 +96,53 @@ struct AttnPlan {
 AttnPlan plan_attn(int B, int S, int H, int D, int window, int nsel, int dtype, bool hca);
 hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, bool hca, hipStream_t stream);
 
+// Projection GEMM C[g][m][n] = sum_k A[g][m][k] * W[g][n][k] (bf16 weights,
+// bf16 or fp32 activations, fp32 accumulation), g < groups.  Requires
+// K % 128 == 0 and N % 16 == 0; pointers 16-byte aligned.
+struct ProjArgs {
+  const void* A;
+  int a_dtype;      // CSA_BF16 or CSA_F32 (split into two bf16 products)
+  int64_t lda;      // elements between token rows of A
+  int64_t a_goff;   // elements between groups of A (along a row)
+  const void* W;    // bf16 [groups][N][K]
+  int64_t w_goff;   // elements between groups of W
+  void* C;
+  int c_dtype;
+  int64_t ldc;
+  int64_t c_goff;
+  int M, N, K, groups;
+  int a_nsum;            // fp32 A: sum of a_nsum partial arrays a_kstride apart
+  int64_t a_kstride;
+  int kc, ks_count;      // K chunk and chunk count (plan_proj)
+  float* part;           // ks_count > 1: fp32 partials [ks][..C layout..]
+  int64_t part_kstride;
+};
+// K chunking of one projection product: token tiles per block (mt), K chunk
+// (kc), chunks (ks) and token chunks.
+struct ProjPlan {
+  int mt, kc, ks, mchunks;
+};
+ProjPlan plan_proj(int M, int N, int K, int groups, bool act_f32);
+hipError_t launch_proj_gemm(const ProjArgs& a, hipStream_t stream);
+// C = sum of the ks_count partials of a (in chunk order).
+hipError_t launch_proj_reduce(const ProjArgs& a, hipStream_t stream);
+
+// Row normalisation y = x / sqrt(mean(x^2) + eps) * gamma over column groups
+// of G, then RoPE of each group's trailing rope_dim at pos[m].
+struct NormArgs {
+  const float* x;
+  int64_t ldx;
+  int x_nsum;          // x is the sum of x_nsum partial arrays x_kstride apart
+  int64_t x_kstride;
+  const float* gamma;  // [G] or null (no gain)
+  const int* pos;      // [M] or null (with rope_dim == 0)
+  void* y;
+  int y_dtype;
+  int64_t ldy;
+  int M, G, rope_dim;
+  double rope_log2_base;
+  float eps;
+};
+hipError_t launch_rows_norm(const NormArgs& a, int ngroups, hipStream_t stream);
+
 }  // namespace csa

@@ -280,6 +280,65 @@ int hca_attn(const void* q, const void* cmp, int Ncap, int ratio,
              int B, int S, int H, int D, void* out, int out_dtype,
              void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * csa_q_proj -- the low-rank query path in front of the attention.
+ *
+ * [V4-Flash walkthrough] "低秩 Q：两次矩阵乘法接起来": for every token m,
+ *   qr   = RMSNorm(x[m] . wq_a^T) * gamma_q          (latent of q_rank)
+ *   q[m] = qr . wq_b^T viewed as H heads of head_dim
+ *   every head divided by its own sqrt(mean(q^2) + eps) (no gain)
+ *   RoPE on the trailing rope_dim dims of every head at position pos[m]
+ * (the Flash widths: d_model 4096, q_rank 1024, 64 heads of 512, RoPE 64).
+ * The latent's RMSNorm carries the learned gain gamma_q (a reading; the page
+ * calls a normalisation layer there).
+ *
+ *   x      [M, d_model] bf16 (token rows; M = B*S)
+ *   wq_a   [q_rank, d_model] bf16;  gamma_q [q_rank] float32
+ *   wq_b   [H*head_dim, q_rank] bf16
+ *   pos    [M] int32 (may be NULL when rope_dim == 0)
+ *   q      [M, H, head_dim] bf16 -- the layout csa_sparse_attn / hca_attn read
+ *   ws     device workspace of csa_q_proj_workspace_size(M, d_model, q_rank,
+ *          H, head_dim) bytes (fp32 partial sums of the products over K
+ *          chunks, the normalised latent), 16-byte aligned, caller-owned.
+ * Requires d_model and q_rank multiples of 128, H*head_dim a multiple of 16,
+ * q_rank <= 16384, and 16-byte aligned x, wq_a, wq_b, q (else
+ * CSA_ERR_UNSUPPORTED / CSA_ERR_INVALID_ARG).  The matrix products run on the
+ * matrix cores with fp32 accumulation; the fp32 latent enters the second
+ * product as a bf16 head plus a bf16 remainder (about 16 significant bits).
+ */
+size_t csa_q_proj_workspace_size(int M, int d_model, int q_rank, int H, int head_dim);
+int csa_q_proj(const void* x, const void* wq_a, const float* gamma_q, const void* wq_b, const int* pos,
+               int M, int d_model, int q_rank, int H, int head_dim, int rope_dim, float rope_base,
+               float eps, void* q, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * csa_out_proj -- the grouped output projection behind the attention.
+ *
+ * [V4-Flash walkthrough] "输出投影也分组，并且降低中间维度": the attention
+ * output o (already rotated back by csa_sparse_attn / hca_attn) is viewed as
+ * `groups` groups of H*head_dim/groups values (group g = heads
+ * g*H/groups .. (g+1)*H/groups - 1); group g goes through its own
+ * down-projection wo_a[g] (o_rank rows), i.e. einsum("bsgd,grd->bsgr"); the
+ * concatenated group results go through wo_b back to d_model
+ * (the Flash widths: 8 groups of 8 heads, o_rank 1024, d_model 4096).
+ *
+ *   o      [M, H, head_dim] (o_dtype: CSA_BF16, or CSA_F32 which enters the
+ *          products as a bf16 head plus a bf16 remainder)
+ *   wo_a   [groups, o_rank, H*head_dim/groups] bf16
+ *   wo_b   [d_model, groups*o_rank] bf16
+ *   y      [M, d_model] (y_dtype)
+ *   ws     device workspace of csa_out_proj_workspace_size(M, H, head_dim,
+ *          groups, o_rank, d_model, o_dtype) bytes (fp32 partial sums of the
+ *          group results and of y over K chunks), 16-byte aligned,
+ *          caller-owned.
+ * Requires H*head_dim/groups and groups*o_rank multiples of 128, o_rank and
+ * d_model multiples of 16, 16-byte aligned o, wo_a, wo_b, y.
+ */
+size_t csa_out_proj_workspace_size(int M, int H, int head_dim, int groups, int o_rank, int d_model, int o_dtype);
+int csa_out_proj(const void* o, int o_dtype, const void* wo_a, const void* wo_b, int M, int H, int head_dim,
+                 int groups, int o_rank, int d_model, void* y, int y_dtype, void* ws, size_t ws_bytes,
+                 hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

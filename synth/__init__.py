@@ -64,14 +64,34 @@ CSA_DECODE_1M = Config("csa_decode_1m", 4, "decode", B=32, ctx=1048576, ctx_lo=5
 # DeepSeek", section 19)
 CSA_DECODE_64K_K1024 = Config("csa_decode_64k_k1024", 5, "decode", B=8, ctx=65536, k=1024)
 
+# one whole attention block at decode: the low-rank query path, the CSA path
+# of csa_decode_64k and the grouped output projection (the Flash widths of
+# ProjDims below)
+ATTN_BLOCK_DECODE_64K = Config("attn_block_decode_64k", 6, "block", B=8, ctx=65536)
+
 CONFIGS = {c.name: c for c in (TINY, CSA_DECODE_64K, HCA_DECODE_1M, CSA_PREFILL_8K, CSA_DECODE_1M,
-                               CSA_DECODE_64K_K1024)}
+                               CSA_DECODE_64K_K1024, ATTN_BLOCK_DECODE_64K)}
 
 # tensor ids of the seeded streams
 T_X, T_WKV, T_WG, T_WKI, T_WGI, T_WQ, T_WQI, T_WW = 0, 1, 2, 3, 4, 5, 6, 7
 T_KV, T_GATE, T_KI, T_GI, T_Q, T_QI, T_W, T_SINK = 10, 11, 12, 13, 14, 15, 16, 17
 T_GAMMA, T_GAMMA_I, T_KVCACHE, T_IDXCACHE, T_WIN, T_LEN, T_SCORES, T_SEL = 20, 21, 22, 23, 24, 25, 26, 27
 T_GAMMA_W = 28
+T_XM, T_WQA, T_GAMMA_Q, T_WQB, T_WOA, T_WOB = 30, 31, 32, 33, 34, 35
+
+
+# Widths of the projections on either side of the attention (the Flash model:
+# "DeepSeek-V4-Flash 架构：一个 token 的旅程", sections "低秩 Q：两次矩阵乘法接起来"
+# and "输出投影也分组，并且降低中间维度").
+@dataclass(frozen=True)
+class ProjDims:
+    d_model: int = 4096
+    q_rank: int = 1024
+    groups: int = 8
+    o_rank: int = 1024
+
+
+FLASH_PROJ = ProjDims()
 
 
 def stream(cid, tid, b=0, chunk=0):
@@ -328,3 +348,31 @@ def random_selection(cid, n_vis, k, b=0, t=0):
     out = np.full(k, -1, np.int32)
     out[:m] = sel
     return out
+
+
+# ---------------------------------------------------------------------------
+# Projection weights and hidden states (random init of the Flash widths)
+# ---------------------------------------------------------------------------
+def proj_weights(cid, H=64, D=512, dims=FLASH_PROJ):
+    """bf16 bits of the query-path and output-projection weights, each drawn
+    N(0, 1/fan_in); the latent's RMSNorm gain 1 + 0.1 N(0,1) (float32).
+
+    wq_a (q_rank, d_model), wq_b (H*D, q_rank), wo_a (groups, o_rank,
+    H*D/groups), wo_b (d_model, groups*o_rank)."""
+    def w(tid, shape, fan_in):
+        x = gaussian(stream(cid, tid), shape)
+        x *= np.float32(1.0 / np.sqrt(fan_in))
+        return bf16_bits(x)
+    hd = H * D
+    return dict(
+        wq_a=w(T_WQA, (dims.q_rank, dims.d_model), dims.d_model),
+        gamma_q=(1.0 + 0.1 * gaussian(stream(cid, T_GAMMA_Q), (dims.q_rank,))).astype(np.float32),
+        wq_b=w(T_WQB, (hd, dims.q_rank), dims.q_rank),
+        wo_a=w(T_WOA, (dims.groups, dims.o_rank, hd // dims.groups), hd // dims.groups),
+        wo_b=w(T_WOB, (dims.d_model, dims.groups * dims.o_rank), dims.groups * dims.o_rank),
+    )
+
+
+def hidden_states(cid, M, d_model, b=0):
+    """Token hidden states x ~ N(0, 1), (M, d_model) bf16 bits."""
+    return bf16_bits(gaussian(stream(cid, T_XM, b), (M, d_model)))

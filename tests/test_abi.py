@@ -231,3 +231,44 @@ def test_misaligned_fast_shapes_are_rejected(lib):
     hws = lib.hca_attn_workspace_size(4, 1, 64, 512, 8192, 128)
     assert lib.hca_attn(MIS, P, 8192, 128, P, 128, 128, P, P, 1, 0.04, 64, 1e4, 4, 1, 64, 512, P, 0, P, hws,
                         None) == INVALID
+
+
+def _qproj(lib, **kw):
+    a = dict(x=P, wq_a=P, gamma=P, wq_b=P, pos=P, M=8, d=4096, r=1024, H=64, hd=512, rope=64, base=10000.0,
+             eps=1e-6, q=P, ws=P, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return lib.csa_q_proj(*a.values())
+
+
+def test_q_proj_validation(lib):
+    # the first product runs in 16 K chunks of 256 (partials summed by the latent's norm), the second in one
+    assert lib.csa_q_proj_workspace_size(8, 4096, 1024, 64, 512) == (16 * 8 * 1024 + 8 * 1024 + 8 * 64 * 512) * 4
+    for bad in (dict(x=None), dict(wq_a=None), dict(gamma=None), dict(wq_b=None), dict(q=None), dict(pos=None),
+                dict(rope=63), dict(rope=514), dict(eps=-1.0), dict(base=0.0), dict(M=-1), dict(H=0),
+                dict(x=MIS), dict(wq_b=MIS), dict(q=MIS)):
+        assert _qproj(lib, **bad) == INVALID, bad
+    assert _qproj(lib, d=4000) == UNSUPPORTED          # K of the first product not a multiple of 128
+    assert _qproj(lib, r=1000) == UNSUPPORTED
+    assert _qproj(lib, ws_bytes=100) == WORKSPACE
+    assert _qproj(lib, ws=None, ws_bytes=0) == WORKSPACE
+    assert _qproj(lib, M=0, ws=None, ws_bytes=0) == 0   # nothing to do, nothing launched
+
+
+def _oproj(lib, **kw):
+    a = dict(o=P, o_dtype=1, wo_a=P, wo_b=P, M=8, H=64, hd=512, G=8, R=1024, d=4096, y=P, y_dtype=0, ws=P,
+             ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return lib.csa_out_proj(*a.values())
+
+
+def test_out_proj_validation(lib):
+    # grouped product in 4 K chunks of 1024, the up-projection in 8 (its partials reduced into y)
+    assert lib.csa_out_proj_workspace_size(8, 64, 512, 8, 1024, 4096, 1) == (4 * 8 * 8192 + 8 * 8 * 4096) * 4
+    for bad in (dict(o=None), dict(wo_a=None), dict(wo_b=None), dict(y=None), dict(o_dtype=3), dict(y_dtype=7),
+                dict(G=7), dict(M=-1), dict(o=MIS), dict(wo_b=MIS), dict(y=MIS)):
+        assert _oproj(lib, **bad) == INVALID, bad
+    assert _oproj(lib, R=1000) == UNSUPPORTED            # o_rank not a multiple of 16
+    assert _oproj(lib, H=64, hd=500, G=8) == UNSUPPORTED  # 4000-wide groups: not a multiple of 128
+    assert _oproj(lib, G=8, R=8) == UNSUPPORTED          # o_rank 8: not a multiple of 16
+    assert _oproj(lib, G=8, R=24) == UNSUPPORTED         # 8 x 24 = 192: K of the second product off 128
+    assert _oproj(lib, ws_bytes=100) == WORKSPACE

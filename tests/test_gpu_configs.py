@@ -49,6 +49,9 @@ def _snapshot(wl):
     """Copies of everything one step writes (for the decode workloads: the
     appended cache rows, not the whole caches)."""
     snap = {"out": wl.out.clone()}
+    for extra in ("q", "y"):          # the attention block's query path and output projection
+        if isinstance(getattr(wl, extra, None), torch.Tensor):
+            snap[extra] = getattr(wl, extra).clone()
     if hasattr(wl, "seqs"):
         e = torch.as_tensor(np.maximum(wl.n_vis - 1, 0), device=wl.out.device)
         b = torch.arange(wl.cfg.B, device=wl.out.device)
@@ -110,7 +113,7 @@ def _stored(entry):
     return oracle.round_bf16(entry)
 
 
-def _check_decode(wl, samples):
+def _check_decode(wl, samples, q_of=None):
     cfg = wl.cfg
     shared = synth.decode_shared(cfg)
     scale = 1.0 / math.sqrt(cfg.D)
@@ -126,7 +129,7 @@ def _check_decode(wl, samples):
         e = s.n_vis - 1
         emitted = (s.pos + 1) % cfg.ratio == 0
         win = np.stack([f64(s.win[p % cfg.window]) for p in oracle.window_positions(s.pos, cfg.window)])
-        q = f64(s.q)
+        q = f64(s.q) if q_of is None else q_of(b)
         if emitted:
             want_kv = _new_entry(cfg, s, shared["gamma"], "kv")
             assert_bf16_matches(host(kv_gpu[b, e])[None], want_kv[None], what=f"b={b} new KV entry")
@@ -234,4 +237,32 @@ def test_csa_prefill_8k():
             cfg.rope_dim, cfg.rope_base)
         assert_attn(out[j], o, what=f"t={t} output")
     assert swaps <= 2
+    _assert_repeatable(wl)
+
+
+def test_attn_block_decode_64k():
+    """One whole attention block at decode (B = 8, 64K context), checked stage
+    by stage against the oracle applied to that stage's GPU inputs: the
+    queries of the low-rank query path (one bf16 ulp or 1e-3 of the head's
+    largest value), the CSA step attending with those GPU queries (as in
+    csa_decode_64k), and the grouped output projection of the GPU's
+    attention output (1e-3 normwise per token)."""
+    import bench
+    cfg = synth.ATTN_BLOCK_DECODE_64K
+    wl = bench.BlockWorkload(cfg, "cuda", copies=1)
+    progress("attn_block_decode_64k: step")
+    _step(wl)
+    dims = wl.dims
+    wts = synth.proj_weights(cfg.cid, cfg.H, cfg.D, dims)
+    x = f64(synth.hidden_states(cfg.cid, cfg.B, dims.d_model))
+    q_gpu = host(wl.q)[:, 0]
+    wq_a, wq_b = f64(wts["wq_a"]), f64(wts["wq_b"])
+    for b in range(cfg.B):
+        want_q = oracle.projection.q_path(x[b], wq_a, wts["gamma_q"], wq_b, cfg.H, cfg.D, int(wl.pos_np[b]),
+                                          cfg.rope_dim, cfg.rope_base, cfg.eps)
+        assert_bf16_matches(q_gpu[b], want_q, what=f"b={b} queries")
+    del wq_a, wq_b
+    assert _check_decode(wl, [0, 4, 7], q_of=lambda b: q_gpu[b]) <= 1
+    want_y = oracle.projection.out_proj(host(wl.out)[:, 0], f64(wts["wo_a"]), f64(wts["wo_b"]), dims.groups)
+    assert_normwise(host(wl.y), want_y, what="block output")
     _assert_repeatable(wl)
