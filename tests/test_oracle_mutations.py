@@ -8,10 +8,11 @@ import pytest
 
 import oracle
 from oracle import csa
-from oracle import projection
+from oracle import projection, quant
 from tests import test_oracle_attention as A
 from tests import test_oracle_pins as P
 from tests import test_oracle_projection as Q
+from tests import test_oracle_quant as QT
 
 _orig = {name: getattr(csa, name) for name in ("pool", "rope", "rms_norm", "index_score", "topk", "attend",
                                                 "window_positions", "sparse_attn", "entry_from_rows")}
@@ -159,7 +160,42 @@ def _out_proj_without_up(o, wo_a, wo_b, groups):
     return y[..., :np.asarray(wo_b).shape[0]]
 
 
+_orig_quant = {name: getattr(quant, name) for name in ("block_scale_exp", "_nearest_code", "quantize_row",
+                                                        "e4m3_decode")}
+
+
+def _scale_clips_like_floor(block, fmt_max):
+    a = float(np.max(np.abs(block)))
+    if a == 0.0:
+        return -127
+    return int(np.floor(np.log2(a))) - int(np.floor(np.log2(fmt_max)))   # the max may exceed the format
+
+
+def _ties_away_from_zero(y, codes, values, sign_bit):
+    y = np.asarray(y, float)
+    d = np.abs(y[..., None] - values)
+    best = np.min(d, axis=-1, keepdims=True)
+    score = (d == best) * (4 + 2 * (((codes & sign_bit) != 0) == np.signbit(y)[..., None]) + np.abs(values) /
+                           (1 + np.max(np.abs(values))))
+    return codes[np.argmax(score, axis=-1)]
+
+
+def _row_nibbles_swapped(v, rope_dim):
+    row = _orig_quant["quantize_row"](v, rope_dim)
+    lat = np.asarray(v).shape[-1] - rope_dim
+    row[:lat // 2] = ((row[:lat // 2] & 15) << 4) | (row[:lat // 2] >> 4)
+    return row
+
+
+def _e4m3_bias_8(code):
+    return _orig_quant["e4m3_decode"](code) / 2.0
+
+
 MUTATIONS = {
+    "quant_scale_may_clip": ("block_scale_exp", _scale_clips_like_floor),
+    "quant_ties_away_from_zero": ("_nearest_code", _ties_away_from_zero),
+    "quant_row_nibbles_swapped": ("quantize_row", _row_nibbles_swapped),
+    "quant_e4m3_exponent_bias_8": ("e4m3_decode", _e4m3_bias_8),
     "q_path_latent_norm_dropped": ("q_path", _q_no_latent_norm),
     "q_path_norm_over_all_heads": ("q_path", _q_norm_over_all_heads),
     "q_path_rope_on_leading_dims": ("q_path", _q_rope_on_leading_dims),
@@ -198,13 +234,16 @@ PINS = [
     Q.test_grouped_projection_is_a_block_diagonal_matmul, Q.test_each_group_reads_only_its_own_heads,
     Q.test_q_path_matches_torch_rms_norm_and_complex_rotation,
     Q.test_q_heads_have_unit_rms_and_rope_spares_the_leading_dims, Q.test_low_rank_query_is_a_two_step_product,
+    QT.test_e4m3_codes_match_torch_float8_e4m3fn, QT.test_e4m3_rounding_matches_torch_conversion,
+    QT.test_e2m1_midpoints_round_to_the_even_code, QT.test_hand_worked_row,
+    lambda: QT.test_block_scale_is_the_smallest_without_clipping("e2m1", 6.0),
 ]
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_planted_mistake_is_caught(name, monkeypatch):
     attr, fn = MUTATIONS[name]
-    mod = projection if attr in _orig_proj else csa
+    mod = projection if attr in _orig_proj else (quant if attr in _orig_quant else csa)
     monkeypatch.setattr(mod, attr, fn)
     if hasattr(oracle, attr):
         monkeypatch.setattr(oracle, attr, fn)
