@@ -31,9 +31,11 @@ Readings (the pages name only the element formats):
   (the code whose lowest bit is 0); a value that rounds to zero keeps its
   sign (the negative-zero code).
 * Row layout (bytes): latent codes, two per byte (even channel in the low
-  nibble); latent scales, one byte per block; tail codes, one byte each;
-  tail scales; zero padding to a multiple of 16 bytes.  D = 512 with a
-  64-wide tail takes 224 + 14 + 64 + 2 = 304 bytes instead of 1024 in bf16.
+  nibble); tail codes, one byte each; latent scales, one byte per block;
+  tail scales; zero padding to a multiple of 16 bytes.  The codes come
+  first so that every group of codes a reader takes at once starts on its
+  own alignment.  D = 512 with a 64-wide tail takes 224 + 64 + 14 + 2 = 304
+  bytes instead of 1024 in bf16.
 """
 from __future__ import annotations
 
@@ -93,7 +95,7 @@ def block_scale_exp(block, fmt_max):
     a = float(np.max(np.abs(block)))
     if a == 0.0:
         return -127
-    x = int(np.ceil(np.log2(a / fmt_max)))
+    x = max(int(np.ceil(np.log2(a / fmt_max))), -127)
     # guard the floating-point log against an off-by-one at exact powers
     while a / 2.0 ** x > fmt_max:
         x += 1
@@ -136,13 +138,12 @@ def quantize_row(v, rope_dim):
     c4, x4 = quantize_blocks(v[:lat], "e2m1")
     out[:lat // 2] = (c4[0::2] | (c4[1::2] << 4)).astype(np.uint8)
     o = lat // 2
-    out[o:o + lat // BLOCK] = (x4 + 127).astype(np.uint8)
-    o += lat // BLOCK
+    s = o + rope_dim                                    # the scale bytes follow all codes
+    out[s:s + lat // BLOCK] = (x4 + 127).astype(np.uint8)
     if rope_dim:
         c8, x8 = quantize_blocks(v[lat:], "e4m3")
         out[o:o + rope_dim] = c8.astype(np.uint8)
-        o += rope_dim
-        out[o:o + rope_dim // BLOCK] = (x8 + 127).astype(np.uint8)
+        out[s + lat // BLOCK:s + lat // BLOCK + rope_dim // BLOCK] = (x8 + 127).astype(np.uint8)
     return out
 
 
@@ -154,12 +155,12 @@ def dequantize_row(row, D, rope_dim):
     c4[0::2] = row[:lat // 2] & 15
     c4[1::2] = row[:lat // 2] >> 4
     o = lat // 2
-    x4 = row[o:o + lat // BLOCK] - 127
-    o += lat // BLOCK
+    s = o + rope_dim
+    x4 = row[s:s + lat // BLOCK] - 127
     out = np.empty(D, dtype=np.float64)
     out[:lat] = dequantize_blocks(c4, x4, "e2m1")
     if rope_dim:
         c8 = row[o:o + rope_dim]
-        x8 = row[o + rope_dim:o + rope_dim + rope_dim // BLOCK] - 127
+        x8 = row[s + lat // BLOCK:s + lat // BLOCK + rope_dim // BLOCK] - 127
         out[lat:] = dequantize_blocks(c8, x8, "e4m3")
     return out
