@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="csa_decode_64k", choices=sorted(synth.CONFIGS))
     ap.add_argument("--extra", default="hca_decode_1m,csa_decode_1m,csa_prefill_8k,csa_decode_64k_k1024,"
-                    "attn_block_decode_64k",
+                    "attn_block_decode_64k,csa_decode_64k_kv4,hca_decode_1m_kv4",
                     help="comma-separated secondary workloads measured after the main one ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -133,6 +133,15 @@ class DecodeWorkload:
         self.copies = copies if cfg.ctx_lo == 0 else 1
         kv0 = torch.zeros((B, self.Ncap, D), dtype=torch.bfloat16, device=device)
         _fill_cache(kv0, cfg.cid, synth.T_KVCACHE, self.n_vis, device)
+        if cfg.kv4:  # the quantised cache of the same rows (quantised by the library itself)
+            import compressed_sparse_attention_06_amd as csa
+            self.kv_row_bytes = csa.csa_kv4_row_bytes(D, cfg.rope_dim)
+            q0 = torch.empty((B, self.Ncap, self.kv_row_bytes), dtype=torch.uint8, device=device)
+            csa.csa_kv4_quantize(kv0, q0, rope_dim=cfg.rope_dim)
+            del kv0
+            kv0 = q0
+        else:
+            self.kv_row_bytes = D * 2
         self.kv = [kv0] + [kv0.clone() for _ in range(self.copies - 1)]
         self.out = torch.empty((B, 1, cfg.H, D), dtype=torch.float32, device=device)
         if cfg.csa:
@@ -213,7 +222,8 @@ class DecodeWorkload:
         rows_in = (1 + cfg.overlap) * cfg.ratio
         vis = self.n_vis
         win = np.minimum(cfg.window, self.pos_np + 1)
-        by = {"compress": emit * (2 * rows_in * D * 2 + D * 2) + D * 4}
+        rb = self.kv_row_bytes  # a compressed KV row: 1 KiB in bf16, 304 B quantised
+        by = {"compress": emit * (2 * rows_in * D * 2 + rb) + D * 4}
         fl = {}
         if cfg.csa:
             by["compress"] += emit * (2 * rows_in * DI * 2 + DI * 2) + DI * 4
@@ -221,22 +231,23 @@ class DecodeWorkload:
             fl["index_score"] = int(np.sum(vis) * HI * DI * 2)
             by["topk"] = int(B * self.Ncap * 4 + B * cfg.k * 4)
             sel = np.minimum(vis, cfg.k)
-            by["sparse_attn"] = int(np.sum((sel + win) * D * 2) + B * (H * D * 2 + cfg.k * 4 + H * D * 4))
+            by["sparse_attn"] = int(np.sum(sel * rb + win * D * 2) + B * (H * D * 2 + cfg.k * 4 + H * D * 4))
             fl["sparse_attn"] = int(np.sum(sel + win) * H * D * 4)
         else:
-            by["hca_attn"] = int(np.sum((vis + win) * D * 2) + B * (H * D * 2 + H * D * 4))
+            by["hca_attn"] = int(np.sum(vis * rb + win * D * 2) + B * (H * D * 2 + H * D * 4))
             fl["hca_attn"] = int(np.sum(vis + win) * H * D * 4)
         return by, fl
 
     def unit(self):
         return "per visible index row: 256 B read (64x128 heads: 16,384 flop)" if self.cfg.csa else \
-            "per attended KV row: 1,024 B read (64 heads x 512: 131,072 flop)"
+            f"per attended KV row: {self.kv_row_bytes:,} B read (64 heads x 512: 131,072 flop)"
 
     def describe(self):
         cfg = self.cfg
         d = dict(workload=cfg.name, batch=cfg.B, context=int(cfg.ctx) if not cfg.ctx_lo else
                  [int(cfg.ctx_lo), int(cfg.ctx)], compressed_entries=int(np.max(self.n_vis)), ratio=cfg.ratio,
-                 heads=cfg.H, head_dim=cfg.D, rope_dim=cfg.rope_dim, window=cfg.window, cache_copies=self.copies)
+                 heads=cfg.H, head_dim=cfg.D, rope_dim=cfg.rope_dim, window=cfg.window, cache_copies=self.copies,
+                 kv_cache="fp4 e2m1 latent + fp8 e4m3 rope tail, 304 B/row" if cfg.kv4 else "bf16, 1024 B/row")
         if cfg.csa:
             d.update(index_heads=cfg.H_I, index_dim=cfg.D_I, top_k=cfg.k)
         return d
@@ -549,10 +560,14 @@ def cpu_baseline_decode(wl, seconds):
     for s in wl.seqs:
         d = dict(seq=s)
         d["kv"] = f64(synth.kv_cache_rows(cfg, s.b, s.n_vis))
+        if cfg.kv4:  # the rows the quantised cache stands for (oracle quantiser), one sequence
+            from oracle import quant
+            d["kv"] = np.stack([quant.dequantize_row(quant.quantize_row(r, cfg.rope_dim), cfg.D, cfg.rope_dim)
+                                for r in d["kv"]])
         if cfg.csa:
             d["idx"] = f64(synth.idx_cache_rows(cfg, s.b, s.n_vis))
         prepared.append(d)
-        if len(prepared) * s.n_vis > 2_000_000:
+        if len(prepared) * s.n_vis > 2_000_000 or cfg.kv4:
             break
 
     def one(d):
@@ -566,6 +581,9 @@ def cpu_baseline_decode(wl, seconds):
             rows = lambda st: f64(st[[t % wl.R for t in toks]])
             d["kv"][e] = oracle.entry_from_rows(e, cfg.ratio, rows(s.gate_stage), rows(s.kv_stage), shared["gamma"],
                                                 cfg.rope_dim, cfg.rope_base, cfg.eps)
+            if cfg.kv4:
+                from oracle import quant
+                d["kv"][e] = quant.dequantize_row(quant.quantize_row(d["kv"][e], cfg.rope_dim), cfg.D, cfg.rope_dim)
         win = np.stack([f64(s.win[p % cfg.window]) for p in oracle.window_positions(s.pos, cfg.window)])
         q = d["q_override"] if "q_override" in d else f64(s.q)
         if cfg.csa:

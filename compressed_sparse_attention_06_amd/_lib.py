@@ -15,7 +15,7 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
 
-CSA_F32, CSA_BF16 = 0, 1
+CSA_F32, CSA_BF16, CSA_KV4 = 0, 1, 2
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape or dtype", -3: "HIP runtime error",
           -4: "workspace too small"}
 
@@ -38,6 +38,8 @@ CSA_MAX_COMPRESS_JOBS = 16
 SIGNATURES = {
     "csa_status_string": (ctypes.c_char_p, [_c_int]),
     "csa_version": (_c_int, []),
+    "csa_kv4_row_bytes": (_c_sz, [_c_int, _c_int]),
+    "csa_kv4_quantize": (_c_int, [_c_p, _c_int, _c_i64, _c_int, _c_int, _c_p, _c_p]),
     "csa_compress_workspace_size": (_c_sz, [_c_i64, _c_int, _c_int, _c_int]),
     "csa_compress": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_int, _c_p, _c_int, _c_int, _c_i64, _c_int, _c_int, _c_int,
                               _c_int, _c_f, _c_f, _c_int, _c_int, _c_int, _c_p, _c_p, _c_int, _c_i64, _c_int, _c_p,
@@ -93,6 +95,8 @@ def _dtype(t):
         return CSA_BF16
     if t.dtype == torch.float32:
         return CSA_F32
+    if t.dtype == torch.uint8:      # a quantised cache: rows of csa_kv4_row_bytes bytes
+        return CSA_KV4
     raise CsaError(f"unsupported tensor dtype {t.dtype}")
 
 
@@ -131,6 +135,22 @@ def _rows(t):
 
 
 # ---------------------------------------------------------------------------
+def csa_kv4_row_bytes(D, rope_dim):
+    return int(lib().csa_kv4_row_bytes(D, rope_dim))
+
+
+def csa_kv4_quantize(x, out, *, rope_dim, stream=None):
+    """x [..., D] (f32 or bf16) -> out [..., csa_kv4_row_bytes(D, rope_dim)] uint8 (quantised cache rows)."""
+    D = x.shape[-1]
+    rows = x.numel() // D
+    _dense(x, out)
+    if out.dtype != torch.uint8 or out.numel() != rows * csa_kv4_row_bytes(D, rope_dim):
+        raise CsaError("out must be a uint8 tensor of rows x csa_kv4_row_bytes(D, rope_dim) bytes")
+    st = lib().csa_kv4_quantize(_ptr(x), _dtype(x), rows, D, rope_dim, _ptr(out), _stream(stream))
+    _check(st, "csa_kv4_quantize")
+    return out
+
+
 def csa_compress_workspace_size(entries, D, ratio, overlap):
     return int(lib().csa_compress_workspace_size(entries, D, ratio, overlap))
 
@@ -148,6 +168,7 @@ def _compress_job(kv, gate, gamma, out, *, ratio, overlap, rope_dim, rope_base=1
     need = csa_compress_workspace_size(B if pos is not None else B * n, D, ratio, overlap)
     if need and (ws is None or _bytes(ws) < need):
         ws = torch.zeros(need, dtype=torch.uint8, device=kv.device)
+    # (a uint8 out is a quantised cache: its batch stride is in bytes)
     job = CompressJob(_ptr(kv), _ptr(gate), _ptr(kv_prev), _ptr(gate_prev), _dtype(kv), _ptr(gamma), B, T, bstride,
                       D, ratio, overlap, rope_dim, rope_base, eps, tok0, e0, n, _ptr(pos), _ptr(out), _dtype(out),
                       _rows(out), out.shape[1], _ptr(ws), _bytes(ws))
@@ -217,6 +238,15 @@ def csa_topk_noalloc(scores, n_valid, k, idx, *, stream=None):
     return idx
 
 
+def _attn_dtype(q, cmp):
+    """The attention's dtype code: CSA_KV4 when cmp holds quantised rows (uint8; q then bf16)."""
+    if cmp.dtype == torch.uint8:
+        if q.dtype != torch.bfloat16:
+            raise CsaError("a quantised cache needs bf16 queries and window rows")
+        return CSA_KV4
+    return _dtype(q)
+
+
 def csa_sparse_attn_workspace_size(B, S, H, D, k, window):
     return int(lib().csa_sparse_attn_workspace_size(B, S, H, D, k, window))
 
@@ -229,7 +259,7 @@ def csa_sparse_attn(q, cmp, idx, win, pos, sink, out, *, window, scale, rope_dim
     _dense(q, cmp, idx, win, pos, sink, out)
     ws = _ws(csa_sparse_attn_workspace_size(B, S, H, D, k, window), ws, q.device)
     st = lib().csa_sparse_attn(_ptr(q), _ptr(cmp), cmp.shape[1], _ptr(idx), k, _ptr(win), win.shape[1], window,
-                               _ptr(pos), _ptr(sink), _dtype(q), scale, rope_dim, rope_base, B, S, H, D, _ptr(out),
+                               _ptr(pos), _ptr(sink), _attn_dtype(q, cmp), scale, rope_dim, rope_base, B, S, H, D, _ptr(out),
                                _dtype(out), _ptr(ws), _bytes(ws), _stream(stream))
     _check(st, "csa_sparse_attn")
     return out
@@ -247,7 +277,7 @@ def hca_attn(q, cmp, win, pos, sink, out, *, ratio, window, scale, rope_dim, rop
     _dense(q, cmp, win, pos, sink, out)
     ws = _ws(hca_attn_workspace_size(B, S, H, D, Ncap, window), ws, q.device)
     st = lib().hca_attn(_ptr(q), _ptr(cmp), Ncap, ratio, _ptr(win), win.shape[1], window, _ptr(pos), _ptr(sink),
-                        _dtype(q), scale, rope_dim, rope_base, B, S, H, D, _ptr(out), _dtype(out), _ptr(ws),
+                        _attn_dtype(q, cmp), scale, rope_dim, rope_base, B, S, H, D, _ptr(out), _dtype(out), _ptr(ws),
                         _bytes(ws), _stream(stream))
     _check(st, "hca_attn")
     return out

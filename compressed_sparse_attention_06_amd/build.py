@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcsa.so")
-SOURCES = ["api.cpp", "compress.hip", "index_score.hip", "topk.hip", "attn.hip", "proj.hip"]
+SOURCES = ["api.cpp", "compress.hip", "index_score.hip", "topk.hip", "attn.hip", "proj.hip", "kv4.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

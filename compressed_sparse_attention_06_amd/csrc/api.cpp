@@ -5,6 +5,7 @@
 
 #include "csa.h"
 #include "kernels.h"
+#include "kv4.h"
 
 namespace {
 
@@ -12,7 +13,9 @@ constexpr int kVersion = 10000;  // 1.0.0
 constexpr int64_t kMaxGridY = 65535;
 
 bool dtype_ok(int d) { return d == CSA_F32 || d == CSA_BF16; }
-int esize(int d) { return d == CSA_BF16 ? 2 : 4; }
+int esize(int d) { return d == CSA_BF16 ? 2 : (d == CSA_KV4 ? 1 : 4); }
+// the quantised row format needs a latent and a tail in whole 32-channel blocks
+bool kv4_shape_ok(int D, int rope_dim) { return D % 32 == 0 && rope_dim % 32 == 0 && rope_dim <= D; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? CSA_OK : CSA_ERR_HIP; }
@@ -46,13 +49,17 @@ namespace {
 // Validates one compressor call and fills its kernel arguments and plan.
 int compress_job(const csa_compress_job& j, csa::CompressArgs* out_args, csa::CompressPlan* out_plan) {
   if (!j.kv || !j.gate || !j.gamma || !j.out) return CSA_ERR_INVALID_ARG;
-  if (!dtype_ok(j.in_dtype) || !dtype_ok(j.out_dtype)) return CSA_ERR_INVALID_ARG;
+  if (!dtype_ok(j.in_dtype) || !(dtype_ok(j.out_dtype) || j.out_dtype == CSA_KV4)) return CSA_ERR_INVALID_ARG;
+  if (j.out_dtype == CSA_KV4 && !kv4_shape_ok(j.D, j.rope_dim)) return CSA_ERR_INVALID_ARG;
   if (j.B < 0 || j.T < 1 || j.D < 1 || j.ratio < 1 || (j.overlap != 0 && j.overlap != 1)) return CSA_ERR_INVALID_ARG;
   if (j.rope_dim < 0 || j.rope_dim % 2 != 0 || j.rope_dim > j.D) return CSA_ERR_INVALID_ARG;
   if (!(j.eps >= 0.f) || !std::isfinite(j.eps) || !(j.rope_base > 0.f) || !std::isfinite(j.rope_base))
     return CSA_ERR_INVALID_ARG;
-  if (j.out_cap < 0 || j.in_bstride < int64_t(j.T) * j.D || j.out_bstride < int64_t(j.out_cap) * j.D)
+  // (a quantised output counts its batch stride in bytes)
+  const int64_t out_row = j.out_dtype == CSA_KV4 ? csa::kv4_row_bytes(j.D, j.rope_dim) : j.D;
+  if (j.out_cap < 0 || j.in_bstride < int64_t(j.T) * j.D || j.out_bstride < int64_t(j.out_cap) * out_row)
     return CSA_ERR_INVALID_ARG;
+  if (j.out_dtype == CSA_KV4 && (!aligned16(j.out) || j.out_bstride % 16 != 0)) return CSA_ERR_INVALID_ARG;
   if (j.D > 8192) return CSA_ERR_UNSUPPORTED;
   if (j.pos == nullptr) {
     if (j.tok0 < 0 || j.e0 < 0 || j.n_entries < 0 || int64_t(j.e0) + j.n_entries > j.out_cap)
@@ -200,7 +207,8 @@ int attn_common(const void* q, const void* cmp, int Ncap, const int* idx, int k,
                 int B, int S, int H, int D, void* out, int out_dtype, void* ws, size_t ws_bytes, bool hca,
                 hipStream_t stream) {
   if (!q || !cmp || !pos || !sink || !out || (!hca && !idx) || (window > 0 && !win)) return CSA_ERR_INVALID_ARG;
-  if (!dtype_ok(dtype) || !dtype_ok(out_dtype)) return CSA_ERR_INVALID_ARG;
+  if (!(dtype_ok(dtype) || dtype == CSA_KV4) || !dtype_ok(out_dtype)) return CSA_ERR_INVALID_ARG;
+  if (dtype == CSA_KV4 && (!kv4_shape_ok(D, rope_dim) || !aligned16(cmp))) return CSA_ERR_INVALID_ARG;
   if (B < 0 || S < 0 || H < 1 || D < 2 || Ncap < 0 || window < 0 || Wcap < window || (!hca && k < 0) ||
       (hca && ratio < 1))
     return CSA_ERR_INVALID_ARG;
@@ -243,6 +251,11 @@ int attn_common(const void* q, const void* cmp, int Ncap, const int* idx, int k,
   a.out = out;
   a.out_dtype = out_dtype;
   a.ws = ws;
+  if (dtype == CSA_KV4) {  // bf16 queries and window rows, quantised compressed rows
+    a.dtype = CSA_BF16;
+    a.cmp_q4 = 1;
+    a.cmp_row_bytes = csa::kv4_row_bytes(D, rope_dim);
+  }
   return hip_status(csa::launch_attn(a, plan, hca, stream));
 }
 
@@ -323,6 +336,20 @@ OPlan o_plan(int M, int groups, int o_rank, int64_t kg, int d_model, bool o_f32)
 }  // namespace
 
 extern "C" {
+
+size_t csa_kv4_row_bytes(int D, int rope_dim) {
+  if (D < 1 || rope_dim < 0 || !kv4_shape_ok(D, rope_dim)) return 0;
+  return size_t(csa::kv4_row_bytes(D, rope_dim));
+}
+
+int csa_kv4_quantize(const void* x, int x_dtype, int64_t rows, int D, int rope_dim, void* out, hipStream_t stream) {
+  if (!x || !out || !dtype_ok(x_dtype) || rows < 0 || D < 1 || rope_dim < 0 || !kv4_shape_ok(D, rope_dim))
+    return CSA_ERR_INVALID_ARG;
+  if (D > 8192 || (rows + 3) / 4 > INT32_MAX) return CSA_ERR_UNSUPPORTED;
+  if (!aligned16(out)) return CSA_ERR_INVALID_ARG;
+  const csa::Kv4Args a{x, x_dtype, rows, D, rope_dim, csa::kv4_row_bytes(D, rope_dim), out};
+  return hip_status(csa::launch_kv4_quantize(a, stream));
+}
 
 size_t csa_q_proj_workspace_size(int M, int d_model, int q_rank, int H, int head_dim) {
   if (M < 0 || d_model < 1 || q_rank < 1 || H < 1 || head_dim < 1) return 0;

@@ -39,6 +39,7 @@
 // unit term is part of the sum and the kernel finishes the output itself.
 #include "common.h"
 #include "kernels.h"
+#include "kv4.h"
 
 namespace csa {
 namespace {
@@ -203,7 +204,7 @@ __device__ __forceinline__ float f16_hi(uint32_t pair) {
 // Matrix-core kernel: grid (B*S, nsplit), 512 threads (8 waves), one
 // workgroup per CU.
 // ---------------------------------------------------------------------------
-template <bool HCA, bool SPLIT>
+template <bool HCA, bool SPLIT, bool Q4>
 __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, int chunk_rows) {
   __shared__ __attribute__((aligned(16))) unsigned char tiles[kBufs][kT * kPitch];
   __shared__ __attribute__((aligned(16))) uint16_t pt[2][kH * kPPitch];
@@ -233,6 +234,19 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
   // candidate: its score is masked, and its finite values keep 0 * row = 0
   const uint16_t* filler = static_cast<const uint16_t*>(a.q) + qi * kH * kD;
 
+  // Quantised compressed rows (Q4): the load unit copies a row's raw bytes
+  // into the start of its tile slot (one copy per row, like a bf16 row), and
+  // the wave that copied it turns it into bf16 in place once the copy has
+  // landed, just before the barrier that publishes the tile.  Lane l takes
+  // channels 8l .. 8l+7.
+  const unsigned char* cmp_q = static_cast<const unsigned char*>(a.cmp) + int64_t(b) * a.Ncap * a.cmp_row_bytes;
+  const bool lane_fp4 = 8 * lane < kD - a.rope_dim;
+  // E2M1 lanes read the 8-byte aligned pair of code words holding theirs
+  const int q_code_off = lane_fp4 ? 8 * (lane / 2) : kv4_code_offset(8 * lane, kD, a.rope_dim);
+  const int q_scale_off = kv4_scale_offset(8 * lane, kD, a.rope_dim);
+  const int q_lanes = a.cmp_row_bytes / 16;  // lanes that copy a raw row, 16 bytes each
+  uint32_t q4mask = 0;  // per tile buffer (4 bits each): the wave's rows that hold raw quantised bytes
+
   // CSA: resolve the chunk's selections once, so that row copies never wait
   // on a dependent index load
   if constexpr (!HCA) {
@@ -254,11 +268,40 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
     if (lane == 0) vmask[buf][wave] = uint8_t(ok & ((1u << kCopyRows) - 1u));
     const uint32_t dst = lds_tiles + uint32_t(buf * kT * kPitch + wave * kCopyRows * kPitch);
     const uint32_t voff = uint32_t(lane ^ (row_flip(wave * kCopyRows) << 3)) * 16u;  // same for the wave's rows
+    uint32_t qm = 0;
 #pragma unroll
     for (int u = 0; u < kCopyRows; ++u) {
       const int cu = __builtin_amdgcn_readlane(code, u);
-      const uint16_t* src = cu >= 0 ? cmp + int64_t(cu) * kD : (cu <= -2 ? win + int64_t(-2 - cu) * kD : filler);
-      copy_row_to_lds(src, voff, dst + uint32_t(u * kPitch));
+      if (Q4 && cu >= 0) {
+        // raw bytes of the quantised row, in order, from the slot's start
+        if (lane < q_lanes) copy_row_to_lds(cmp_q + int64_t(cu) * a.cmp_row_bytes, uint32_t(lane) * 16u,
+                                            dst + uint32_t(u * kPitch));
+        qm |= 1u << u;
+      } else {
+        const uint16_t* src = cu >= 0 ? cmp + int64_t(cu) * kD : (cu <= -2 ? win + int64_t(-2 - cu) * kD : filler);
+        copy_row_to_lds(src, voff, dst + uint32_t(u * kPitch));
+      }
+    }
+    if constexpr (Q4) q4mask = (q4mask & ~(15u << (4 * buf))) | (qm << (4 * buf));
+  };
+  // Q4: the wave's quantised rows of tile t, turned into bf16 in place (each
+  // lane reads its code bytes and scale byte, then writes its 16-byte chunk
+  // where a bf16 row copy would have put it; a row's reads all happen before
+  // its writes, so the overlap is harmless)
+  auto dequant_tile = [&](int t) {
+    const int buf = t % kBufs;
+    const uint32_t qm = (q4mask >> (4 * buf)) & 15u;
+    if (qm == 0) return;
+    unsigned char* slot0 = &tiles[buf][0] + wave * kCopyRows * kPitch;
+    const int chunk = (lane ^ (row_flip(wave * kCopyRows) << 3)) * 16;
+#pragma unroll
+    for (int u = 0; u < kCopyRows; ++u) {
+      if (!((qm >> u) & 1u)) continue;
+      unsigned char* slot = slot0 + u * kPitch;
+      uint2 cw = *reinterpret_cast<const uint2*>(slot + q_code_off);
+      const uint32_t sb = slot[q_scale_off];
+      if (lane_fp4) cw.x = (lane & 1) ? cw.y : cw.x;
+      *reinterpret_cast<uint4*>(slot + chunk) = kv4_lane_bf16(cw, sb, lane_fp4);
     }
   };
   // The first min(n_tiles, kBufs) tiles are copied up front (every buffer is
@@ -275,6 +318,9 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
     else if (later == 2) wait_vmem<2 * kCopyRows>();
     else if (later == 1) wait_vmem<kCopyRows>();
     else wait_vmem<0>();
+    if constexpr (Q4) {
+      if (s < n_tiles) dequant_tile(s);  // this wave's copies of tile s have landed
+    }
     __syncthreads();
     if (s + 2 >= kBufs && s + 2 < n_tiles) issue(s + 2);
   };
@@ -1046,12 +1092,14 @@ __device__ __forceinline__ void attn_head(const AttnArgs a, int64_t qi, int h, f
     const int64_t off = cand_row(a, HCA, c, qi, b, j, &fw);
     if (off < 0) continue;
     const void* src = fw ? a.win : a.cmp;
+    const bool q4 = !fw && a.cmp_q4;  // a quantised compressed row: row index off / D
+    const unsigned char* qrow = static_cast<const unsigned char*>(a.cmp) + (off / D) * a.cmp_row_bytes;
     float rowv[kMaxPer];
     float dot = 0.f;
 #pragma unroll
     for (int i = 0; i < kMaxPer; ++i) {
       const int d = lane + i * kWave;
-      rowv[i] = d < D ? load_elem(src, a.dtype, off + d) : 0.f;
+      rowv[i] = d < D ? (q4 ? kv4_elem(qrow, d, D, a.rope_dim) : load_elem(src, a.dtype, off + d)) : 0.f;
       dot += q[i] * rowv[i];
     }
     const float s = wave_sum(dot) * qk_scale;
@@ -1111,7 +1159,7 @@ __global__ __launch_bounds__(kWave) void attn_redo(AttnArgs a, const int* redo) 
 
 AttnPlan plan_attn(int B, int S, int H, int D, int window, int nsel, int dtype, bool hca) {
   AttnPlan p{false, false, 1, 0, 0};
-  p.mfma = dtype == CSA_BF16 && H == kH && D == kD;
+  p.mfma = (dtype == CSA_BF16 || dtype == CSA_KV4) && H == kH && D == kD;
   if (!p.mfma) return p;
   const int64_t max_cand = int64_t(window) + nsel;
   const int64_t nq = int64_t(B) * S;
@@ -1133,7 +1181,8 @@ AttnPlan plan_attn(int B, int S, int H, int D, int window, int nsel, int dtype, 
   }
   if (p.nsplit > 1) {
     p.ws_bytes = size_t(nq) * p.nsplit * (size_t(kPartialVecs) * 16 + kH * 4 * sizeof(float));
-  } else if (nq >= kPersistMinQueries && (hca || nsel <= kPMaxSel)) {
+  } else if (nq >= kPersistMinQueries && (hca || nsel <= kPMaxSel) && dtype != CSA_KV4) {
+    // (quantised caches take one workgroup per query instead)
     p.persist = true;
     p.ws_bytes = size_t(nq) * sizeof(int);  // per-query recompute flags
   }
@@ -1159,10 +1208,20 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, bool hca, hipStr
   } else if (plan.mfma) {
     const dim3 grid(unsigned(nq), plan.nsplit);
     const bool split = plan.nsplit > 1;
-    if (hca && split) hipLaunchKernelGGL((attn_mfma<true, true>), grid, dim3(kThreads), 0, stream, a, plan.nsplit, plan.chunk_rows);
-    else if (hca) hipLaunchKernelGGL((attn_mfma<true, false>), grid, dim3(kThreads), 0, stream, a, plan.nsplit, plan.chunk_rows);
-    else if (split) hipLaunchKernelGGL((attn_mfma<false, true>), grid, dim3(kThreads), 0, stream, a, plan.nsplit, plan.chunk_rows);
-    else hipLaunchKernelGGL((attn_mfma<false, false>), grid, dim3(kThreads), 0, stream, a, plan.nsplit, plan.chunk_rows);
+#define CSA_ATTN_MFMA(H_, S_, Q_) \
+  hipLaunchKernelGGL((attn_mfma<H_, S_, Q_>), grid, dim3(kThreads), 0, stream, a, plan.nsplit, plan.chunk_rows)
+    if (a.cmp_q4) {
+      if (hca && split) CSA_ATTN_MFMA(true, true, true);
+      else if (hca) CSA_ATTN_MFMA(true, false, true);
+      else if (split) CSA_ATTN_MFMA(false, true, true);
+      else CSA_ATTN_MFMA(false, false, true);
+    } else {
+      if (hca && split) CSA_ATTN_MFMA(true, true, false);
+      else if (hca) CSA_ATTN_MFMA(true, false, false);
+      else if (split) CSA_ATTN_MFMA(false, true, false);
+      else CSA_ATTN_MFMA(false, false, false);
+    }
+#undef CSA_ATTN_MFMA
     if (plan.nsplit > 1)
       hipLaunchKernelGGL(attn_combine, dim3(unsigned(nq), kPartialVecs / kWave), dim3(256),
                          size_t(3) * plan.nsplit * 16 * sizeof(float), stream, a, plan.nsplit);

@@ -16,6 +16,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "kv4.h"
 
 namespace csa {
 namespace {
@@ -69,6 +70,13 @@ __device__ __forceinline__ Task compress_task(const CompressArgs& a, int w) {
     t.live = t.e < a.out_cap;
   }
   return t;
+}
+
+// Quantised output: entry e of sequence b at out + b*out_bstride bytes + e
+// rows of kv4_row_bytes.
+__device__ __forceinline__ unsigned char* kv4_out_row(const CompressArgs& a, int b, int e) {
+  return static_cast<unsigned char*>(a.out) + int64_t(b) * a.out_bstride +
+         int64_t(e) * kv4_row_bytes(a.D, a.rope_dim);
 }
 
 // Row of token `tok` inside a sequence's span (span mode) or ring (ring mode).
@@ -341,21 +349,32 @@ __global__ __launch_bounds__(kWave* max_waves(CPL)) void compress_lanes(Compress
   const int64_t o = int64_t(task.b) * a.out_bstride + int64_t(e) * D;
 
   if (gr == 1) {
-    if (!active) return;
     // the lane's own channels, rotated in place (RoPE pairs never straddle
     // lanes) and stored with one vector store
+    if (active) {
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) y[i] *= inv_rms * gam[i];
+      for (int i = 0; i < CPL; ++i) y[i] *= inv_rms * gam[i];
 #pragma unroll
-    for (int i = 0; i < CPL; i += 2) {
-      const int ch = c0 + i;
-      if (ch >= rope0) {
-        const float cs = rope_tab[ch - rope0], sn = rope_tab[ch - rope0 + 1];
-        const float x0 = y[i], x1 = y[i + 1];
-        y[i] = x0 * cs - x1 * sn;
-        y[i + 1] = x0 * sn + x1 * cs;
+      for (int i = 0; i < CPL; i += 2) {
+        const int ch = c0 + i;
+        if (ch >= rope0) {
+          const float cs = rope_tab[ch - rope0], sn = rope_tab[ch - rope0 + 1];
+          const float x0 = y[i], x1 = y[i + 1];
+          y[i] = x0 * cs - x1 * sn;
+          y[i + 1] = x0 * sn + x1 * cs;
+        }
       }
     }
+    if (a.out_dtype == CSA_KV4) {  // quantised cache row: staged in LDS, written by wave 0
+      if (active) {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) ybuf[c0 + i] = y[i];
+      }
+      __syncthreads();
+      if (wave == 0) kv4_store_row(ybuf, D, a.rope_dim, kv4_out_row(a, task.b, e));
+      return;
+    }
+    if (!active) return;
     if (a.out_dtype == CSA_BF16) {
       uint32_t* dst = static_cast<uint32_t*>(a.out) + (o + c0) / 2;
       if constexpr (CPL == 8)
@@ -382,10 +401,18 @@ __global__ __launch_bounds__(kWave* max_waves(CPL)) void compress_lanes(Compress
       y0 = x0 * cs - x1 * sn;
       y1 = x0 * sn + x1 * cs;
     }
-    if (a.out_dtype == CSA_BF16)
+    if (a.out_dtype == CSA_KV4) {  // in place: this thread alone reads and writes the pair
+      ybuf[ch] = y0;
+      ybuf[ch + 1] = y1;
+    } else if (a.out_dtype == CSA_BF16) {
       static_cast<uint32_t*>(a.out)[(o + ch) / 2] = pack_bf16x2(y0, y1);
-    else
+    } else {
       *reinterpret_cast<float2*>(static_cast<float*>(a.out) + o + ch) = float2{y0, y1};
+    }
+  }
+  if (a.out_dtype == CSA_KV4) {
+    __syncthreads();
+    if (wave == 0) kv4_store_row(ybuf, D, a.rope_dim, kv4_out_row(a, task.b, e));
   }
 }
 
@@ -433,6 +460,10 @@ __global__ __launch_bounds__(kWave) void compress_any(CompressArgs a) {
     ybuf[rope0 + 2 * i + 1] = x0 * sn + x1 * cs;
   }
   __syncthreads();
+  if (a.out_dtype == CSA_KV4) {
+    kv4_store_row(ybuf, D, a.rope_dim, kv4_out_row(a, task.b, e));
+    return;
+  }
   const int64_t o = int64_t(task.b) * a.out_bstride + int64_t(e) * D;
   for (int c = lane; c < D; c += kWave) store_elem(a.out, a.out_dtype, o + c, ybuf[c]);
 }
@@ -480,7 +511,7 @@ int job_tasks(const CompressArgs& a) { return a.pos == nullptr ? a.B * a.n_entri
 
 bool lanes_ready(const CompressArgs& a, const CompressPlan& p) {
   auto al = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
-  const int in_es = a.in_dtype == CSA_BF16 ? 2 : 4, out_es = a.out_dtype == CSA_BF16 ? 2 : 4;
+  const int in_es = a.in_dtype == CSA_BF16 ? 2 : 4, out_es = a.out_dtype == CSA_BF16 ? 2 : (a.out_dtype == CSA_KV4 ? 1 : 4);
   return p.lanes && al(a.kv) && al(a.gate) && al(a.kv_prev) && al(a.gate_prev) && al(a.out) &&
          (a.in_bstride * in_es) % 16 == 0 && (a.out_bstride * out_es) % 16 == 0;
 }

@@ -85,6 +85,8 @@ struct AttnArgs {
   void* out;
   int out_dtype;
   void* ws;
+  int cmp_q4;         // cmp rows are quantised (kv4.h); q and win are then bf16
+  int cmp_row_bytes;  // bytes per quantised cmp row
 };
 struct AttnPlan {
   bool mfma;
@@ -95,6 +97,16 @@ struct AttnPlan {
 };
 AttnPlan plan_attn(int B, int S, int H, int D, int window, int nsel, int dtype, bool hca);
 hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, bool hca, hipStream_t stream);
+
+// Quantisation of rows into the FP4/FP8 cache format of kv4.h.
+struct Kv4Args {
+  const void* x;
+  int x_dtype;
+  int64_t rows;
+  int D, rope_dim, row_bytes;
+  void* out;
+};
+hipError_t launch_kv4_quantize(const Kv4Args& a, hipStream_t stream);
 
 // Projection GEMM C[g][m][n] = sum_k A[g][m][k] * W[g][n][k] (bf16 weights,
 // bf16 or fp32 activations, fp32 accumulation), g < groups.  Requires

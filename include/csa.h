@@ -48,7 +48,11 @@
 extern "C" {
 #endif
 
-enum { CSA_F32 = 0, CSA_BF16 = 1 };
+/* CSA_KV4: the quantised compressed-KV row format (FP4 E2M1 latent, FP8 E4M3
+ * RoPE tail, one power-of-two scale per 32 channels; see csa_kv4_quantize).
+ * It is a cache format only: csa_compress may write it, csa_sparse_attn and
+ * hca_attn read it (their queries and window rows stay bf16). */
+enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_KV4 = 2 };
 
 enum {
   CSA_OK = 0,
@@ -63,6 +67,31 @@ const char* csa_status_string(int status);
 
 /* Library version, major*10000 + minor*100 + patch. */
 int csa_version(void);
+
+/*
+ * csa_kv4_row_bytes / csa_kv4_quantize -- the quantised compressed-KV cache.
+ *
+ * [V4.1 lab] "3 Giải pháp": the cache budget is priced with FP4 E2M1 for the
+ * latent and FP8 E4M3 for the RoPE tail; [LLM Atlas] "FP8 训练真正难在哪":
+ * low precision takes fine-grained scaling.  The block scaling and the byte
+ * layout are this library's reading (the pages give neither):
+ *   row = [latent codes: (D-rope_dim)/2 bytes, two per byte, even channel in
+ *          the low nibble] [tail codes: rope_dim bytes] [one scale byte per
+ *          32 channels, latent blocks first: the block scale is 2^(byte-127),
+ *          the smallest power of two that brings the block's largest
+ *          magnitude within 6 (E2M1) or 448 (E4M3)] [zeros to 16 bytes];
+ *   elements round to the nearest code, ties to the even code, and a value
+ *   rounding to zero keeps its sign.
+ * D = 512 with a 64-wide tail: 304 bytes per row (1024 in bf16).
+ *
+ * csa_kv4_row_bytes returns the row size, or 0 when D or rope_dim is not a
+ * multiple of 32 (the format needs whole blocks).
+ * csa_kv4_quantize writes rows [rows, row_bytes] (out, 16-byte aligned) from
+ * x [rows, D] (x_dtype CSA_F32 or CSA_BF16).
+ */
+size_t csa_kv4_row_bytes(int D, int rope_dim);
+int csa_kv4_quantize(const void* x, int x_dtype, int64_t rows, int D, int rope_dim, void* out,
+                     hipStream_t stream);
 
 /*
  * csa_compress -- build compressed entries from per-token rows.
@@ -84,7 +113,11 @@ int csa_version(void);
  *   gamma             [D] float32 RMSNorm weight.
  *   ratio >= 1, overlap in {0,1}, rope_dim even and <= D, eps >= 0.
  *   out               [B, out_cap, D] (out_dtype); entry e of sequence b is
- *                     written at out + (b*out_bstride + e*D) elements.
+ *                     written at out + (b*out_bstride + e*D) elements.  With
+ *                     out_dtype CSA_KV4 the entry is written quantised:
+ *                     out_bstride counts bytes (a multiple of 16) and entry e
+ *                     is the row at out + b*out_bstride + e*csa_kv4_row_bytes
+ *                     bytes (D and rope_dim multiples of 32).
  *
  *   Span mode (pos == NULL): row j of each sequence holds token tok0 + j,
  *     0 <= j < T.  Entries e0 .. e0+n_entries-1 are written for every
@@ -248,7 +281,10 @@ int csa_topk_noalloc(const float* scores, const int* n_valid, int R, int N, int 
  *   q [B,S,H,D] (dtype), cmp [B,Ncap,D] (dtype), idx [B,S,k] int32,
  *   win [B,Wcap,D] (dtype), pos [B,S] int32, sink [H] float32,
  *   out [B,S,H,D] (out_dtype).  A prefill passes its per-token window rows
- *   with Wcap >= the largest position + 1.
+ *   with Wcap >= the largest position + 1.  dtype CSA_KV4: q and win are
+ *   bf16 and cmp holds quantised rows [B, Ncap, csa_kv4_row_bytes(D,
+ *   rope_dim)] bytes, dequantised exactly to bf16 on the way into the
+ *   products (D and rope_dim multiples of 32).
  * Matrix-core path: dtype CSA_BF16, H == 64, D == 512; q, cmp, win and out
  * must then be 16-byte aligned (else CSA_ERR_INVALID_ARG).  Other shapes run
  * a vector-ALU path (D <= 1024).  ws: csa_sparse_attn_workspace_size bytes,

@@ -50,6 +50,7 @@ class Config:
     eps: float = 1e-6
     rope_base: float = 10000.0
     dtype: str = "bf16"
+    kv4: bool = False    # compressed KV cache stored quantised (FP4 latent, FP8 RoPE tail)
 
 
 TINY = Config("tiny_csa", 0, "tiny", B=1, H=2, D=32, rope_dim=8, H_I=2, D_I=16,
@@ -69,8 +70,14 @@ CSA_DECODE_64K_K1024 = Config("csa_decode_64k_k1024", 5, "decode", B=8, ctx=6553
 # ProjDims below)
 ATTN_BLOCK_DECODE_64K = Config("attn_block_decode_64k", 6, "block", B=8, ctx=65536)
 
+# the two decode workloads with the quantised compressed-KV cache ("Lab tổng hợp
+# DeepSeek-V4.1-Flash", section "3 Giải pháp": FP4 E2M1 latent, FP8 E4M3 tail)
+CSA_DECODE_64K_KV4 = Config("csa_decode_64k_kv4", 7, "decode", B=8, ctx=65536, kv4=True)
+HCA_DECODE_1M_KV4 = Config("hca_decode_1m_kv4", 8, "decode", B=4, ctx=1048576, ratio=128, overlap=0, csa=False,
+                           kv4=True)
+
 CONFIGS = {c.name: c for c in (TINY, CSA_DECODE_64K, HCA_DECODE_1M, CSA_PREFILL_8K, CSA_DECODE_1M,
-                               CSA_DECODE_64K_K1024, ATTN_BLOCK_DECODE_64K)}
+                               CSA_DECODE_64K_K1024, ATTN_BLOCK_DECODE_64K, CSA_DECODE_64K_KV4, HCA_DECODE_1M_KV4)}
 
 # tensor ids of the seeded streams
 T_X, T_WKV, T_WG, T_WKI, T_WGI, T_WQ, T_WQI, T_WW = 0, 1, 2, 3, 4, 5, 6, 7

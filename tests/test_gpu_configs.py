@@ -90,9 +90,9 @@ def _gpu_set_attention(cfg, b, got_sel, want_kv, emitted, e):
     set (equal to the oracle's up to legal swaps), with the appended entry
     replaced by the oracle's own value."""
     picked = [int(i) for i in got_sel if i >= 0]
-    rows = f64(synth.kv_cache_rows_at(cfg, b, picked)) if picked else np.zeros((0, cfg.D))
+    rows = _cache_stand_in(cfg, synth.kv_cache_rows_at(cfg, b, picked)) if picked else np.zeros((0, cfg.D))
     if emitted and e in picked:
-        rows[picked.index(e)] = _stored(want_kv)
+        rows[picked.index(e)] = _stored(want_kv, cfg)
     return rows
 
 
@@ -108,9 +108,20 @@ def _new_entry(cfg, s, gamma, role):
     return oracle.entry_from_rows(e, cfg.ratio, f64(g[slots]), f64(v[slots]), gamma, rd, cfg.rope_base, cfg.eps)
 
 
-def _stored(entry):
-    """The entry as the bf16 cache holds it."""
+def _stored(entry, cfg=None):
+    """The entry as the cache holds it: bf16, or the values of its quantised row."""
+    if cfg is not None and cfg.kv4:
+        return oracle.quant.dequantize_row(oracle.quant.quantize_row(entry, cfg.rope_dim), cfg.D, cfg.rope_dim)
     return oracle.round_bf16(entry)
+
+
+def _cache_stand_in(cfg, rows):
+    """Values the pre-filled cache rows stand for (quantised by the oracle's
+    quantiser when the workload keeps a quantised cache)."""
+    rows = f64(rows)
+    if cfg.kv4:
+        return np.stack([_stored(r, cfg) for r in rows]) if len(rows) else rows
+    return rows
 
 
 def _check_decode(wl, samples, q_of=None):
@@ -132,11 +143,15 @@ def _check_decode(wl, samples, q_of=None):
         q = f64(s.q) if q_of is None else q_of(b)
         if emitted:
             want_kv = _new_entry(cfg, s, shared["gamma"], "kv")
-            assert_bf16_matches(host(kv_gpu[b, e])[None], want_kv[None], what=f"b={b} new KV entry")
+            if cfg.kv4:
+                from tests.test_gpu_kv4 import _band_equal
+                _band_equal(kv_gpu[b, e].cpu().numpy(), want_kv, cfg.rope_dim, f"b={b} new KV entry")
+            else:
+                assert_bf16_matches(host(kv_gpu[b, e])[None], want_kv[None], what=f"b={b} new KV entry")
         if not cfg.csa:
-            cmp = f64(synth.kv_cache_rows(cfg, b, s.n_vis))
+            cmp = _cache_stand_in(cfg, synth.kv_cache_rows(cfg, b, s.n_vis))
             if emitted:
-                cmp[e] = _stored(want_kv)
+                cmp[e] = _stored(want_kv, cfg)
             want = oracle.hca_attn(q, cmp, s.n_vis, win, shared["sink"], scale, s.pos, cfg.rope_dim, cfg.rope_base)
             assert_attn(out[b, 0], want, what=f"b={b} HCA output")
             continue
@@ -197,6 +212,29 @@ def test_csa_decode_1m_lengths_mix():
     progress("csa_decode_1m: step")
     _step(wl)
     assert _check_decode(wl, [0, 7, 19, 31]) <= 1
+    _assert_repeatable(wl)
+
+
+def test_csa_decode_64k_kv4():
+    """The 64K-context CSA decode with the quantised compressed-KV cache
+    (304 B per row): the appended entry quantised by the compressor, the
+    attention over the selected quantised rows."""
+    import bench
+    wl = bench.DecodeWorkload(synth.CSA_DECODE_64K_KV4, "cuda", copies=1)
+    progress("csa_decode_64k_kv4: step")
+    _step(wl)
+    assert _check_decode(wl, [0, 6]) <= 1
+    _assert_repeatable(wl)
+
+
+def test_hca_decode_1m_kv4():
+    """The 1M-context HCA decode over a quantised cache of 8,192 rows per
+    sequence (two sequences checked: the oracle quantises every row)."""
+    import bench
+    wl = bench.DecodeWorkload(synth.HCA_DECODE_1M_KV4, "cuda", copies=1)
+    progress("hca_decode_1m_kv4: step")
+    _step(wl)
+    _check_decode(wl, [0, 3])
     _assert_repeatable(wl)
 
 
