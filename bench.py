@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="csa_decode_64k", choices=sorted(synth.CONFIGS))
     ap.add_argument("--extra", default="hca_decode_1m,csa_decode_1m,csa_prefill_8k,csa_decode_64k_k1024,"
-                    "attn_block_decode_64k,csa_decode_64k_kv4,hca_decode_1m_kv4",
+                    "attn_block_decode_64k,csa_decode_64k_kv4,hca_decode_1m_kv4,csa_decode_1m_paged",
                     help="comma-separated secondary workloads measured after the main one ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -326,6 +326,119 @@ class BlockWorkload(DecodeWorkload):
         return d
 
 
+class PagedDecodeWorkload(DecodeWorkload):
+    """The decode step with both compressed caches in shared page pools.
+
+    The page allocator (csa_page_pool) starts from a shuffled free list and
+    hands pages out a round at a time to every sequence that still needs one,
+    as concurrent sequences growing together would get them; each sequence
+    holds the pages its visible entries (and this step's append) need, so the
+    pools hold the visible rows only instead of every sequence's full
+    capacity.  The kernels are the paged entry points; the seeded rows are the
+    contiguous workload's."""
+
+    def __init__(self, cfg, device, copies=COPIES, batch=None):
+        import torch
+        import compressed_sparse_attention_06_amd as csa
+        super().__init__(cfg, device, copies=copies, batch=batch)
+        cfg, B, pr = self.cfg, self.cfg.B, self.cfg.page_rows
+        self.page_rows = pr
+        self.max_pages = (self.Ncap + pr - 1) // pr
+        need = np.maximum(self.n_vis, self.pos_np // cfg.ratio + 1)   # entries this step may touch
+        pages = (need + pr - 1) // pr
+        self.pool_pages = int(pages.sum())
+        self.alloc = csa.PagePool(self.pool_pages)
+        free = self.alloc.alloc(self.pool_pages)
+        self.alloc.release(np.random.default_rng(cfg.cid).permutation(free))
+        tab = np.full((B, self.max_pages), -1, np.int32)
+        for rnd in range(int(pages.max())):
+            for b in range(B):
+                if rnd < pages[b]:
+                    self.alloc.reserve(tab[b], pr, int(min(need[b], (rnd + 1) * pr)))
+        assert self.alloc.available() == 0
+        self.table_np = tab
+        self.table = torch.from_numpy(tab).to(device)
+
+        def paginate(caches):
+            out = []
+            for cache in caches:
+                W = cache.shape[2]
+                pool = torch.zeros((self.pool_pages * pr, W), dtype=cache.dtype, device=device)
+                for b in range(B):
+                    n = int(pages[b])
+                    dst = (torch.from_numpy(tab[b, :n]).to(device).long()[:, None] * pr +
+                           torch.arange(pr, device=device)[None]).view(-1)
+                    rows = min(n * pr, self.Ncap)
+                    pool[dst[:rows]] = cache[b, :rows]
+                out.append(pool)
+            return out
+
+        self.kv = paginate(self.kv)
+        if cfg.csa:
+            self.idx_cache = paginate(self.idx_cache)
+            self.scores = torch.empty((B, 1, self.max_pages * pr), dtype=torch.float32, device=device)
+            self.ws_topk = torch.empty(max(1, csa.csa_topk_workspace_size(B, self.max_pages * pr, cfg.k)),
+                                       dtype=torch.uint8, device=device)
+        torch.cuda.synchronize()
+
+    def launches(self, c):
+        import compressed_sparse_attention_06_amd as csa
+        cfg, pr = self.cfg, self.page_rows
+        c = c % self.copies
+        scale = 1.0 / math.sqrt(cfg.D)
+        N = self.max_pages * pr
+        kv_job = dict(kv=self.kv_stage, gate=self.gate_stage, gamma=self.gamma, pool=self.kv[c], pages=self.table,
+                      page_rows=pr, ratio=cfg.ratio, overlap=cfg.overlap, rope_dim=cfg.rope_dim,
+                      rope_base=cfg.rope_base, eps=cfg.eps, pos=self.pos, ws=self.ws_ckv)
+        if not cfg.csa:
+            return [("compress", lambda: csa.csa_compress_paged(**kv_job)),
+                    ("hca_attn", lambda: csa.hca_attn_paged(
+                        self.q, self.kv[c], self.table, self.win, self.pos2, self.sink, self.out, page_rows=pr,
+                        ratio=cfg.ratio, window=cfg.window, scale=scale, rope_dim=cfg.rope_dim,
+                        rope_base=cfg.rope_base, ws=self.ws_attn))]
+        idx_job = dict(kv=self.ki_stage, gate=self.gi_stage, gamma=self.gamma_idx, pool=self.idx_cache[c],
+                       pages=self.table, page_rows=pr, ratio=cfg.ratio, overlap=cfg.overlap,
+                       rope_dim=cfg.rope_dim_idx, rope_base=cfg.rope_base, eps=cfg.eps, pos=self.pos, ws=self.ws_cidx)
+        return [
+            ("compress", lambda: (csa.csa_compress_paged(**kv_job), csa.csa_compress_paged(**idx_job))),
+            ("index_score", lambda: csa.csa_index_score_paged(self.q_idx, self.w, self.idx_cache[c], self.pos2,
+                                                              self.scores, self.table, page_rows=pr,
+                                                              ratio=cfg.ratio)),
+            ("topk", lambda: csa.csa_topk(self.scores.view(cfg.B, N), None, cfg.k, self.sel.view(cfg.B, cfg.k),
+                                          ws=self.ws_topk)),
+            ("sparse_attn", lambda: csa.csa_sparse_attn_paged(
+                self.q, self.kv[c], self.table, self.sel, self.win, self.pos2, self.sink, self.out, page_rows=pr,
+                window=cfg.window, scale=scale, rope_dim=cfg.rope_dim, rope_base=cfg.rope_base, ws=self.ws_attn)),
+        ]
+
+    def algorithmic(self):
+        """The contiguous step's bytes plus the page-table entries read: one
+        per page of visible index rows, one per selected or attended row."""
+        by, fl = super().algorithmic()
+        cfg = self.cfg
+        N = self.max_pages * self.page_rows
+        vis = self.n_vis
+        if cfg.csa:
+            by["index_score"] += int(np.sum((vis + self.page_rows - 1) // self.page_rows) * 4)
+            by["index_score"] += int(cfg.B * (N - self.Ncap) * 4)
+            by["topk"] += int(cfg.B * (N - self.Ncap) * 4)
+            by["sparse_attn"] += int(np.sum(np.minimum(vis, cfg.k)) * 4)
+        else:
+            by["hca_attn"] += int(np.sum((vis + self.page_rows - 1) // self.page_rows) * 4)
+        return by, fl
+
+    def describe(self):
+        d = super().describe()
+        d.update(page_rows=self.page_rows, pool_pages=self.pool_pages,
+                 pool_gib=round(self.pool_pages * self.page_rows * (self.kv_row_bytes +
+                                                                    (self.cfg.D_I * 2 if self.cfg.csa else 0)) /
+                                2 ** 30, 2),
+                 contiguous_gib=round(self.cfg.B * self.Ncap * (self.kv_row_bytes +
+                                                                (self.cfg.D_I * 2 if self.cfg.csa else 0)) / 2 ** 30,
+                                      2))
+        return d
+
+
 class PrefillWorkload:
     """CSA prefill of S tokens: compress all groups, score, top-k, attention."""
 
@@ -431,7 +544,7 @@ class PrefillWorkload:
 def make_workload(name, device):
     cfg = synth.CONFIGS[name]
     if cfg.kind == "decode":
-        return DecodeWorkload(cfg, device)
+        return PagedDecodeWorkload(cfg, device) if cfg.page_rows else DecodeWorkload(cfg, device)
     if cfg.kind == "block":
         return BlockWorkload(cfg, device)
     if cfg.kind == "prefill":
@@ -794,7 +907,8 @@ def main():
         m2 = measure(w2, args.steps, args.warmup)
         note(f"{name}: {m2['ms_per_step'] * 1e3:.2f} us/step")
         extras[name] = summary(w2, m2)
-        if not args.no_cpu_baseline:
+        # (a paged workload computes what its contiguous twin does: no second oracle timing)
+        if not args.no_cpu_baseline and not w2.cfg.page_rows:
             extras[name]["cpu_baseline"] = cpu_baseline(w2, args.cpu_seconds / 2)
             note(f"{name} cpu baseline: {extras[name]['cpu_baseline']['value']:.2f} query-tokens/s")
         del w2

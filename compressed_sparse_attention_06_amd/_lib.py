@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
 
 CSA_F32, CSA_BF16, CSA_KV4 = 0, 1, 2
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape or dtype", -3: "HIP runtime error",
-          -4: "workspace too small"}
+          -4: "workspace too small", -5: "out of pages"}
 
 _c_int, _c_i64, _c_f, _c_sz, _c_p = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 
@@ -34,6 +34,12 @@ class CompressJob(ctypes.Structure):
 
 CSA_MAX_COMPRESS_JOBS = 16
 
+
+class PageTableC(ctypes.Structure):
+    """csa_page_table of include/csa.h."""
+    _fields_ = [("pages", _c_p), ("max_pages", _c_int), ("page_rows", _c_int), ("pool_pages", _c_int)]
+
+
 # name -> (restype, argtypes); mirrors include/csa.h
 SIGNATURES = {
     "csa_status_string": (ctypes.c_char_p, [_c_int]),
@@ -45,6 +51,22 @@ SIGNATURES = {
                               _c_int, _c_f, _c_f, _c_int, _c_int, _c_int, _c_p, _c_p, _c_int, _c_i64, _c_int, _c_p,
                               _c_sz, _c_p]),
     "csa_compress_jobs": (_c_int, [ctypes.POINTER(CompressJob), _c_int, _c_p]),
+    "csa_compress_paged": (_c_int, [ctypes.POINTER(CompressJob), ctypes.POINTER(PageTableC), _c_p]),
+    "csa_index_score_paged": (_c_int, [_c_p, _c_p, _c_p, _c_int, _c_p, _c_int, _c_int, _c_int, _c_int,
+                                       ctypes.POINTER(PageTableC), _c_int, _c_p, _c_p]),
+    "csa_sparse_attn_paged": (_c_int, [_c_p, _c_p, ctypes.POINTER(PageTableC), _c_p, _c_int, _c_p, _c_int, _c_int,
+                                       _c_p, _c_p, _c_int, _c_f, _c_int, _c_f, _c_int, _c_int, _c_int, _c_int, _c_p,
+                                       _c_int, _c_p, _c_sz, _c_p]),
+    "hca_attn_paged": (_c_int, [_c_p, _c_p, ctypes.POINTER(PageTableC), _c_int, _c_p, _c_int, _c_int, _c_p, _c_p,
+                                _c_int, _c_f, _c_int, _c_f, _c_int, _c_int, _c_int, _c_int, _c_p, _c_int, _c_p, _c_sz,
+                                _c_p]),
+    "csa_page_pool_create": (_c_p, [_c_int]),
+    "csa_page_pool_destroy": (None, [_c_p]),
+    "csa_page_pool_available": (_c_int, [_c_p]),
+    "csa_page_pool_alloc": (_c_int, [_c_p, _c_int, _c_p]),
+    "csa_page_pool_release": (_c_int, [_c_p, _c_int, _c_p]),
+    "csa_page_table_reserve": (_c_int, [_c_p, _c_p, _c_int, _c_int, _c_i64]),
+    "csa_page_table_release": (_c_int, [_c_p, _c_p, _c_int]),
     "csa_index_score": (_c_int, [_c_p, _c_p, _c_p, _c_int, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                  _c_p, _c_p]),
     "csa_topk_workspace_size": (_c_sz, [_c_int, _c_int, _c_int]),
@@ -319,3 +341,117 @@ def csa_out_proj(o, wo_a, wo_b, y, *, ws=None, stream=None):
                             _dtype(y), _ptr(ws), _bytes(ws), _stream(stream))
     _check(st, "csa_out_proj")
     return y
+
+
+# ---------------------------------------------------------------------------
+# Paged caches and the page allocator
+# ---------------------------------------------------------------------------
+def _page_table(pages, page_rows, pool):
+    """csa_page_table for a device int32 [B, max_pages] table over `pool` (rows of the cache)."""
+    _dense(pages)
+    if pages.dtype != torch.int32 or pages.dim() != 2:
+        raise CsaError("pages must be an int32 [B, max_pages] device tensor")
+    return PageTableC(_ptr(pages), pages.shape[1], page_rows, pool.shape[0] // page_rows)
+
+
+def csa_compress_paged(kv, gate, gamma, pool, pages, *, page_rows, ratio, overlap, rope_dim, rope_base=10000.0,
+                       eps=1e-6, kv_prev=None, gate_prev=None, tok0=0, e0=0, n_entries=None, pos=None, ws=None,
+                       stream=None):
+    """csa_compress into a paged cache: pool [pool_rows, D] (or uint8 [pool_rows, row_bytes] quantised),
+    pages [B, max_pages] int32.  Span mode needs n_entries."""
+    B, T, D = kv.shape
+    bstride = _rows(kv)
+    _dense(gamma, pos, pool)
+    if pos is None and n_entries is None:
+        raise CsaError("span mode needs n_entries")
+    n = 0 if n_entries is None else n_entries
+    need = csa_compress_workspace_size(B if pos is not None else B * n, D, ratio, overlap)
+    if need and (ws is None or _bytes(ws) < need):
+        ws = torch.zeros(need, dtype=torch.uint8, device=kv.device)
+    job = CompressJob(_ptr(kv), _ptr(gate), _ptr(kv_prev), _ptr(gate_prev), _dtype(kv), _ptr(gamma), B, T, bstride,
+                      D, ratio, overlap, rope_dim, rope_base, eps, tok0, e0, n, _ptr(pos), _ptr(pool), _dtype(pool),
+                      0, 0, _ptr(ws), _bytes(ws))
+    pt = _page_table(pages, page_rows, pool)
+    st = lib().csa_compress_paged(ctypes.byref(job), ctypes.byref(pt), _stream(stream))
+    _check(st, "csa_compress_paged")
+    return pool
+
+
+def csa_index_score_paged(q_idx, w, idx_pool, pos, scores, pages, *, page_rows, ratio, stream=None):
+    """scores [B,S,max_pages*page_rows] f32 from a paged index cache idx_pool [pool_rows, D_I]."""
+    B, S, H, D = q_idx.shape
+    _dense(q_idx, w, idx_pool, pos, scores)
+    pt = _page_table(pages, page_rows, idx_pool)
+    st = lib().csa_index_score_paged(_ptr(q_idx), _ptr(w), _ptr(idx_pool), _dtype(q_idx), _ptr(pos), B, S, H, D,
+                                     ctypes.byref(pt), ratio, _ptr(scores), _stream(stream))
+    _check(st, "csa_index_score_paged")
+    return scores
+
+
+def csa_sparse_attn_paged(q, cmp_pool, pages, idx, win, pos, sink, out, *, page_rows, window, scale, rope_dim,
+                          rope_base=10000.0, ws=None, stream=None):
+    B, S, H, D = q.shape
+    k = idx.shape[-1]
+    _dense(q, cmp_pool, idx, win, pos, sink, out)
+    pt = _page_table(pages, page_rows, cmp_pool)
+    ws = _ws(csa_sparse_attn_workspace_size(B, S, H, D, k, window), ws, q.device)
+    st = lib().csa_sparse_attn_paged(_ptr(q), _ptr(cmp_pool), ctypes.byref(pt), _ptr(idx), k, _ptr(win),
+                                     win.shape[1], window, _ptr(pos), _ptr(sink), _attn_dtype(q, cmp_pool), scale,
+                                     rope_dim, rope_base, B, S, H, D, _ptr(out), _dtype(out), _ptr(ws), _bytes(ws),
+                                     _stream(stream))
+    _check(st, "csa_sparse_attn_paged")
+    return out
+
+
+def hca_attn_paged(q, cmp_pool, pages, win, pos, sink, out, *, page_rows, ratio, window, scale, rope_dim,
+                   rope_base=10000.0, ws=None, stream=None):
+    B, S, H, D = q.shape
+    _dense(q, cmp_pool, win, pos, sink, out)
+    pt = _page_table(pages, page_rows, cmp_pool)
+    ws = _ws(hca_attn_workspace_size(B, S, H, D, pages.shape[1] * page_rows, window), ws, q.device)
+    st = lib().hca_attn_paged(_ptr(q), _ptr(cmp_pool), ctypes.byref(pt), ratio, _ptr(win), win.shape[1], window,
+                              _ptr(pos), _ptr(sink), _attn_dtype(q, cmp_pool), scale, rope_dim, rope_base, B, S, H, D,
+                              _ptr(out), _dtype(out), _ptr(ws), _bytes(ws), _stream(stream))
+    _check(st, "hca_attn_paged")
+    return out
+
+
+class PagePool:
+    """The library's page allocator (csa_page_pool): which pages of a device pool are free.
+
+    Tables are host int32 numpy rows (-1 = no page); upload them to the device for the kernels."""
+
+    def __init__(self, n_pages):
+        self._h = lib().csa_page_pool_create(n_pages)
+        if not self._h:
+            raise CsaError("csa_page_pool_create failed")
+        self.n_pages = n_pages
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h and _lib is not None:
+            _lib.csa_page_pool_destroy(h)
+
+    def available(self):
+        return int(lib().csa_page_pool_available(self._h))
+
+    def alloc(self, n):
+        import numpy as np
+        out = np.empty(max(n, 1), dtype=np.int32)
+        _check(lib().csa_page_pool_alloc(self._h, n, out.ctypes.data), "csa_page_pool_alloc")
+        return out[:n]
+
+    def release(self, pages):
+        import numpy as np
+        arr = np.ascontiguousarray(pages, dtype=np.int32)
+        _check(lib().csa_page_pool_release(self._h, arr.size, arr.ctypes.data), "csa_page_pool_release")
+
+    def reserve(self, row, page_rows, n_entries):
+        """Make the host table row (int32 numpy, modified in place) cover n_entries entries."""
+        _check(lib().csa_page_table_reserve(self._h, row.ctypes.data, row.size, page_rows, n_entries),
+               "csa_page_table_reserve")
+        return row
+
+    def release_row(self, row):
+        _check(lib().csa_page_table_release(self._h, row.ctypes.data, row.size), "csa_page_table_release")
+        return row

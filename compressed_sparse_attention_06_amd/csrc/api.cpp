@@ -2,6 +2,9 @@
 // and dispatch to the gfx950 kernels.  See include/csa.h for the contract.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
+#include <new>
+#include <vector>
 
 #include "csa.h"
 #include "kernels.h"
@@ -31,6 +34,7 @@ const char* csa_status_string(int status) {
     case CSA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case CSA_ERR_HIP: return "HIP runtime error";
     case CSA_ERR_WORKSPACE: return "workspace too small";
+    case CSA_ERR_NO_PAGES: return "out of pages";
     default: return "unknown status";
   }
 }
@@ -46,8 +50,23 @@ size_t csa_compress_workspace_size(int64_t entries, int D, int ratio, int overla
 
 namespace {
 
+// A caller's page table, validated: page_rows a power of two >= 64, the
+// logical capacity max_pages*page_rows within int32.
+int page_table(const csa_page_table* t, csa::PageTable* out) {
+  if (t == nullptr || t->pages == nullptr || t->max_pages < 1 || t->pool_pages < 1) return CSA_ERR_INVALID_ARG;
+  if (t->page_rows < 64 || t->page_rows > (1 << 20) || (t->page_rows & (t->page_rows - 1)) != 0)
+    return CSA_ERR_INVALID_ARG;
+  if (int64_t(t->max_pages) * t->page_rows > INT32_MAX || int64_t(t->pool_pages) * t->page_rows > INT32_MAX)
+    return CSA_ERR_UNSUPPORTED;
+  int shift = 0;
+  while ((1 << shift) < t->page_rows) ++shift;
+  *out = csa::PageTable{t->pages, t->max_pages, shift, t->pool_pages};
+  return CSA_OK;
+}
+
 // Validates one compressor call and fills its kernel arguments and plan.
-int compress_job(const csa_compress_job& j, csa::CompressArgs* out_args, csa::CompressPlan* out_plan) {
+int compress_job(const csa_compress_job& j, csa::CompressArgs* out_args, csa::CompressPlan* out_plan,
+                 const csa::PageTable* pt = nullptr) {
   if (!j.kv || !j.gate || !j.gamma || !j.out) return CSA_ERR_INVALID_ARG;
   if (!dtype_ok(j.in_dtype) || !(dtype_ok(j.out_dtype) || j.out_dtype == CSA_KV4)) return CSA_ERR_INVALID_ARG;
   if (j.out_dtype == CSA_KV4 && !kv4_shape_ok(j.D, j.rope_dim)) return CSA_ERR_INVALID_ARG;
@@ -57,9 +76,11 @@ int compress_job(const csa_compress_job& j, csa::CompressArgs* out_args, csa::Co
     return CSA_ERR_INVALID_ARG;
   // (a quantised output counts its batch stride in bytes)
   const int64_t out_row = j.out_dtype == CSA_KV4 ? csa::kv4_row_bytes(j.D, j.rope_dim) : j.D;
-  if (j.out_cap < 0 || j.in_bstride < int64_t(j.T) * j.D || j.out_bstride < int64_t(j.out_cap) * out_row)
+  // (a paged output ignores out_bstride: its rows live in the pool)
+  if (j.out_cap < 0 || j.in_bstride < int64_t(j.T) * j.D || (pt == nullptr && j.out_bstride < int64_t(j.out_cap) * out_row))
     return CSA_ERR_INVALID_ARG;
-  if (j.out_dtype == CSA_KV4 && (!aligned16(j.out) || j.out_bstride % 16 != 0)) return CSA_ERR_INVALID_ARG;
+  if (j.out_dtype == CSA_KV4 && (!aligned16(j.out) || (pt == nullptr && j.out_bstride % 16 != 0)))
+    return CSA_ERR_INVALID_ARG;
   if (j.D > 8192) return CSA_ERR_UNSUPPORTED;
   if (j.pos == nullptr) {
     if (j.tok0 < 0 || j.e0 < 0 || j.n_entries < 0 || int64_t(j.e0) + j.n_entries > j.out_cap)
@@ -112,6 +133,10 @@ int compress_job(const csa_compress_job& j, csa::CompressArgs* out_args, csa::Co
   a.out_bstride = j.out_bstride;
   a.out_cap = j.out_cap;
   a.ws = j.ws;
+  if (pt != nullptr) {
+    a.pt = *pt;
+    a.out_bstride = 0;
+  }
   *out_args = a;
   *out_plan = plan;
   return CSA_OK;
@@ -136,6 +161,20 @@ int csa_compress(const void* kv, const void* gate, const void* kv_prev, const vo
   return hip_status(csa::launch_compress(&a, &plan, 1, stream));
 }
 
+int csa_compress_paged(const csa_compress_job* job, const csa_page_table* out_pages, hipStream_t stream) {
+  if (job == nullptr) return CSA_ERR_INVALID_ARG;
+  csa::PageTable pt;
+  int st = page_table(out_pages, &pt);
+  if (st != CSA_OK) return st;
+  csa_compress_job j = *job;
+  j.out_cap = out_pages->max_pages * out_pages->page_rows;  // the logical capacity of a sequence
+  csa::CompressArgs a;
+  csa::CompressPlan plan;
+  st = compress_job(j, &a, &plan, &pt);
+  if (st != CSA_OK) return st;
+  return hip_status(csa::launch_compress(&a, &plan, 1, stream));
+}
+
 int csa_compress_jobs(const csa_compress_job* jobs, int n_jobs, hipStream_t stream) {
   if (n_jobs < 0 || n_jobs > CSA_MAX_COMPRESS_JOBS || (n_jobs > 0 && jobs == nullptr)) return CSA_ERR_INVALID_ARG;
   csa::CompressArgs a[CSA_MAX_COMPRESS_JOBS];
@@ -147,8 +186,12 @@ int csa_compress_jobs(const csa_compress_job* jobs, int n_jobs, hipStream_t stre
   return hip_status(csa::launch_compress(a, plan, n_jobs, stream));
 }
 
-int csa_index_score(const void* q_idx, const float* w, const void* idx_cache, int dtype, const int* pos, int B,
-                    int S, int H_I, int D_I, int Ncap, int ratio, float* scores, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int index_common(const void* q_idx, const float* w, const void* idx_cache, int dtype, const int* pos, int B, int S,
+                 int H_I, int D_I, int Ncap, int ratio, float* scores, const csa::PageTable* pt, hipStream_t stream) {
   if (!q_idx || !w || !idx_cache || !pos || !scores) return CSA_ERR_INVALID_ARG;
   if (!dtype_ok(dtype) || B < 0 || S < 0 || H_I < 1 || D_I < 1 || Ncap < 0 || ratio < 1) return CSA_ERR_INVALID_ARG;
   if (int64_t(B) * S > INT32_MAX || (int64_t(Ncap) + 255) / 256 > kMaxGridY) return CSA_ERR_UNSUPPORTED;
@@ -171,7 +214,27 @@ int csa_index_score(const void* q_idx, const float* w, const void* idx_cache, in
   a.Ncap = Ncap;
   a.ratio = ratio;
   a.scores = scores;
+  if (pt != nullptr) a.pt = *pt;
   return hip_status(csa::launch_index_score(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa_index_score(const void* q_idx, const float* w, const void* idx_cache, int dtype, const int* pos, int B,
+                    int S, int H_I, int D_I, int Ncap, int ratio, float* scores, hipStream_t stream) {
+  return index_common(q_idx, w, idx_cache, dtype, pos, B, S, H_I, D_I, Ncap, ratio, scores, nullptr, stream);
+}
+
+int csa_index_score_paged(const void* q_idx, const float* w, const void* idx_pool, int dtype, const int* pos, int B,
+                          int S, int H_I, int D_I, const csa_page_table* pages, int ratio, float* scores,
+                          hipStream_t stream) {
+  csa::PageTable pt;
+  const int st = page_table(pages, &pt);
+  if (st != CSA_OK) return st;
+  return index_common(q_idx, w, idx_pool, dtype, pos, B, S, H_I, D_I, pages->max_pages * pages->page_rows, ratio,
+                      scores, &pt, stream);
 }
 
 size_t csa_topk_workspace_size(int R, int N, int k) {
@@ -205,7 +268,7 @@ namespace {
 int attn_common(const void* q, const void* cmp, int Ncap, const int* idx, int k, int ratio, const void* win, int Wcap,
                 int window, const int* pos, const float* sink, int dtype, float scale, int rope_dim, float rope_base,
                 int B, int S, int H, int D, void* out, int out_dtype, void* ws, size_t ws_bytes, bool hca,
-                hipStream_t stream) {
+                hipStream_t stream, const csa::PageTable* pt = nullptr) {
   if (!q || !cmp || !pos || !sink || !out || (!hca && !idx) || (window > 0 && !win)) return CSA_ERR_INVALID_ARG;
   if (!(dtype_ok(dtype) || dtype == CSA_KV4) || !dtype_ok(out_dtype)) return CSA_ERR_INVALID_ARG;
   if (dtype == CSA_KV4 && (!kv4_shape_ok(D, rope_dim) || !aligned16(cmp))) return CSA_ERR_INVALID_ARG;
@@ -218,7 +281,7 @@ int attn_common(const void* q, const void* cmp, int Ncap, const int* idx, int k,
   if (int64_t(B) * S > INT32_MAX) return CSA_ERR_UNSUPPORTED;
   const int64_t max_cand = int64_t(window) + (hca ? Ncap : k);
   if (max_cand > INT32_MAX) return CSA_ERR_UNSUPPORTED;
-  csa::AttnPlan plan = csa::plan_attn(B, S, H, D, window, hca ? Ncap : k, dtype, hca);
+  csa::AttnPlan plan = csa::plan_attn(B, S, H, D, window, hca ? Ncap : k, dtype, hca, pt != nullptr);
   // matrix-core shape: rows travel in 16-byte pieces, so misaligned tensors
   // are rejected (not run on the vector path)
   if (plan.mfma && !(aligned16(q) && aligned16(cmp) && (window == 0 || aligned16(win)) && aligned16(out)))
@@ -256,12 +319,20 @@ int attn_common(const void* q, const void* cmp, int Ncap, const int* idx, int k,
     a.cmp_q4 = 1;
     a.cmp_row_bytes = csa::kv4_row_bytes(D, rope_dim);
   }
+  if (pt != nullptr) a.pt = *pt;
   return hip_status(csa::launch_attn(a, plan, hca, stream));
 }
 
+// enough for every plan of the shape: bf16 or quantised, contiguous or paged
 size_t attn_ws(int B, int S, int H, int D, int window, int nsel, bool hca) {
   if (B < 0 || S < 0 || H < 1 || D < 2 || window < 0 || nsel < 0 || int64_t(window) + nsel > INT32_MAX) return 0;
-  return csa::plan_attn(B, S, H, D, window, nsel, CSA_BF16, hca).ws_bytes;
+  size_t ws = 0;
+  for (int dt : {CSA_BF16, CSA_KV4})
+    for (bool paged : {false, true}) {
+      const size_t w = csa::plan_attn(B, S, H, D, window, nsel, dt, hca, paged).ws_bytes;
+      ws = w > ws ? w : ws;
+    }
+  return ws;
 }
 
 }  // namespace
@@ -289,6 +360,118 @@ int hca_attn(const void* q, const void* cmp, int Ncap, int ratio, const void* wi
              int H, int D, void* out, int out_dtype, void* ws, size_t ws_bytes, hipStream_t stream) {
   return attn_common(q, cmp, Ncap, nullptr, 0, ratio, win, Wcap, window, pos, sink, dtype, scale, rope_dim,
                      rope_base, B, S, H, D, out, out_dtype, ws, ws_bytes, true, stream);
+}
+
+int csa_sparse_attn_paged(const void* q, const void* cmp_pool, const csa_page_table* pages, const int* idx, int k,
+                          const void* win, int Wcap, int window, const int* pos, const float* sink, int dtype,
+                          float scale, int rope_dim, float rope_base, int B, int S, int H, int D, void* out,
+                          int out_dtype, void* ws, size_t ws_bytes, hipStream_t stream) {
+  csa::PageTable pt;
+  const int st = page_table(pages, &pt);
+  if (st != CSA_OK) return st;
+  return attn_common(q, cmp_pool, pages->max_pages * pages->page_rows, idx, k, 1, win, Wcap, window, pos, sink, dtype,
+                     scale, rope_dim, rope_base, B, S, H, D, out, out_dtype, ws, ws_bytes, false, stream, &pt);
+}
+
+int hca_attn_paged(const void* q, const void* cmp_pool, const csa_page_table* pages, int ratio, const void* win,
+                   int Wcap, int window, const int* pos, const float* sink, int dtype, float scale, int rope_dim,
+                   float rope_base, int B, int S, int H, int D, void* out, int out_dtype, void* ws, size_t ws_bytes,
+                   hipStream_t stream) {
+  csa::PageTable pt;
+  const int st = page_table(pages, &pt);
+  if (st != CSA_OK) return st;
+  return attn_common(q, cmp_pool, pages->max_pages * pages->page_rows, nullptr, 0, ratio, win, Wcap, window, pos, sink,
+                     dtype, scale, rope_dim, rope_base, B, S, H, D, out, out_dtype, ws, ws_bytes, true, stream, &pt);
+}
+
+// ---------------------------------------------------------------------------
+// Page pool: which pages of a caller-owned device pool are free (host only)
+// ---------------------------------------------------------------------------
+struct csa_page_pool {
+  std::mutex mu;
+  std::vector<int> free_pages;  // a stack: the lowest-numbered free page on top after creation
+  std::vector<unsigned char> used;
+};
+
+csa_page_pool* csa_page_pool_create(int n_pages) {
+  if (n_pages < 1) return nullptr;
+  csa_page_pool* p = new (std::nothrow) csa_page_pool;
+  if (p == nullptr) return nullptr;
+  try {
+    p->free_pages.resize(size_t(n_pages));
+    for (int i = 0; i < n_pages; ++i) p->free_pages[size_t(i)] = n_pages - 1 - i;
+    p->used.assign(size_t(n_pages), 0);
+  } catch (...) {
+    delete p;
+    return nullptr;
+  }
+  return p;
+}
+
+void csa_page_pool_destroy(csa_page_pool* pool) { delete pool; }
+
+int csa_page_pool_available(csa_page_pool* pool) {
+  if (pool == nullptr) return CSA_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(pool->mu);
+  return int(pool->free_pages.size());
+}
+
+int csa_page_pool_alloc(csa_page_pool* pool, int n, int* pages) {
+  if (pool == nullptr || n < 0 || (n > 0 && pages == nullptr)) return CSA_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(pool->mu);
+  if (size_t(n) > pool->free_pages.size()) return CSA_ERR_NO_PAGES;
+  for (int i = 0; i < n; ++i) {
+    pages[i] = pool->free_pages.back();
+    pool->free_pages.pop_back();
+    pool->used[size_t(pages[i])] = 1;
+  }
+  return CSA_OK;
+}
+
+int csa_page_pool_release(csa_page_pool* pool, int n, const int* pages) {
+  if (pool == nullptr || n < 0 || (n > 0 && pages == nullptr)) return CSA_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(pool->mu);
+  // all or nothing: every page must be in use and named once
+  std::vector<unsigned char> seen;
+  for (int i = 0; i < n; ++i) {
+    const int pg = pages[i];
+    if (pg < 0 || size_t(pg) >= pool->used.size() || !pool->used[size_t(pg)]) return CSA_ERR_INVALID_ARG;
+    if (seen.empty()) seen.assign(pool->used.size(), 0);
+    if (seen[size_t(pg)]) return CSA_ERR_INVALID_ARG;
+    seen[size_t(pg)] = 1;
+  }
+  for (int i = n - 1; i >= 0; --i) {
+    pool->used[size_t(pages[i])] = 0;
+    pool->free_pages.push_back(pages[i]);
+  }
+  return CSA_OK;
+}
+
+int csa_page_table_reserve(csa_page_pool* pool, int* row, int max_pages, int page_rows, int64_t n_entries) {
+  if (pool == nullptr || row == nullptr || max_pages < 1 || page_rows < 1 || n_entries < 0) return CSA_ERR_INVALID_ARG;
+  const int64_t need = (n_entries + page_rows - 1) / page_rows;
+  if (need > max_pages) return CSA_ERR_INVALID_ARG;
+  int missing = 0;
+  for (int64_t j = 0; j < need; ++j) missing += row[j] < 0 ? 1 : 0;
+  if (missing == 0) return CSA_OK;
+  std::vector<int> got(size_t(missing), -1);
+  const int st = csa_page_pool_alloc(pool, missing, got.data());
+  if (st != CSA_OK) return st;  // nothing taken
+  int k = 0;
+  for (int64_t j = 0; j < need; ++j)
+    if (row[j] < 0) row[j] = got[size_t(k++)];
+  return CSA_OK;
+}
+
+int csa_page_table_release(csa_page_pool* pool, int* row, int max_pages) {
+  if (pool == nullptr || row == nullptr || max_pages < 1) return CSA_ERR_INVALID_ARG;
+  std::vector<int> held;
+  for (int j = 0; j < max_pages; ++j)
+    if (row[j] >= 0) held.push_back(row[j]);
+  const int st = csa_page_pool_release(pool, int(held.size()), held.data());
+  if (st != CSA_OK) return st;
+  for (int j = 0; j < max_pages; ++j) row[j] = -1;
+  return CSA_OK;
 }
 
 }  // extern "C"

@@ -149,11 +149,15 @@ __device__ __forceinline__ int64_t cand_row(const AttnArgs& a, bool hca, const C
   if (i >= c.n_sel) return -1;
   const int64_t e = hca ? i : int64_t(a.idx[qi * a.k + i]);
   if (e < 0 || e >= a.Ncap) return -1;
+  if (a.pt.pages) {
+    const int64_t r = paged_row(a.pt, b, e);
+    return r < 0 ? -1 : r * a.D;
+  }
   return (int64_t(b) * a.Ncap + e) * a.D;
 }
 
-// Candidate code: >= 0 compressed entry, <= -2 window ring slot (-2 - slot),
-// -1 no row.
+// Candidate code: >= 0 compressed row (the entry, or its pool row in a paged
+// cache), <= -2 window ring slot (-2 - slot), -1 no row.
 __device__ __forceinline__ int cand_code(const AttnArgs& a, bool hca, const Cand& c, int64_t qi, int64_t j) {
   if (j < c.n_win) {
     const int slot = c.s0 + int(j);  // j < window <= Wcap: at most one wrap
@@ -162,7 +166,9 @@ __device__ __forceinline__ int cand_code(const AttnArgs& a, bool hca, const Cand
   const int64_t i = j - c.n_win;
   if (i >= c.n_sel) return -1;
   const int64_t e = hca ? i : int64_t(a.idx[qi * a.k + i]);
-  return (e >= 0 && e < a.Ncap) ? int(e) : -1;
+  if (e < 0 || e >= a.Ncap) return -1;
+  if (a.pt.pages) return int(paged_row(a.pt, int(qi / a.S), e));  // -1 when unallocated
+  return int(e);
 }
 
 // Split partials.  Split (qi, split) stores, per head h, its part of the
@@ -213,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
   __shared__ float mseen[2][kH];
   __shared__ float mref[kH];  // reference of the current pass, per head
   __shared__ int over_flag;
-  __shared__ int codes[HCA ? 1 : kMaxChunk];
+  __shared__ int codes[kMaxChunk];  // resolved candidate codes (HCA: only for a paged cache)
   __shared__ float amax[SPLIT ? 4 : 1][kH];  // split partials: largest |O|/l per PV wave and head
   __shared__ float escale[SPLIT ? kH : 1];   // split partials: the head's exponent e
 
@@ -229,7 +235,8 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
   const int n_rows = int(j_begin < n_cand ? (n_cand - j_begin < chunk_rows ? n_cand - j_begin : chunk_rows) : 0);
   const int n_tiles = (n_rows + kT - 1) / kT;
   const uint16_t* win = static_cast<const uint16_t*>(a.win) + int64_t(b) * a.Wcap * kD;
-  const uint16_t* cmp = static_cast<const uint16_t*>(a.cmp) + int64_t(b) * a.Ncap * kD;
+  // candidate codes are pool rows when the cache is paged
+  const uint16_t* cmp = static_cast<const uint16_t*>(a.cmp) + (a.pt.pages ? 0 : int64_t(b) * a.Ncap * kD);
   // a readable 1 KiB row (the query's first head) stands in for a missing
   // candidate: its score is masked, and its finite values keep 0 * row = 0
   const uint16_t* filler = static_cast<const uint16_t*>(a.q) + qi * kH * kD;
@@ -239,7 +246,8 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
   // the wave that copied it turns it into bf16 in place once the copy has
   // landed, just before the barrier that publishes the tile.  Lane l takes
   // channels 8l .. 8l+7.
-  const unsigned char* cmp_q = static_cast<const unsigned char*>(a.cmp) + int64_t(b) * a.Ncap * a.cmp_row_bytes;
+  const unsigned char* cmp_q =
+      static_cast<const unsigned char*>(a.cmp) + (a.pt.pages ? 0 : int64_t(b) * a.Ncap * a.cmp_row_bytes);
   const bool lane_fp4 = 8 * lane < kD - a.rope_dim;
   // E2M1 lanes read the 8-byte aligned pair of code words holding theirs
   const int q_code_off = lane_fp4 ? 8 * (lane / 2) : kv4_code_offset(8 * lane, kD, a.rope_dim);
@@ -249,8 +257,9 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
 
   // CSA: resolve the chunk's selections once, so that row copies never wait
   // on a dependent index load
-  if constexpr (!HCA) {
-    for (int j = tid; j < n_rows; j += kThreads) codes[j] = cand_code(a, false, c, qi, j_begin + j);
+  const bool resolved = !HCA || a.pt.pages != nullptr;  // HCA: contiguous rows need no table
+  if (resolved) {
+    for (int j = tid; j < n_rows; j += kThreads) codes[j] = cand_code(a, HCA, c, qi, j_begin + j);
   }
   if (tid == 0) over_flag = 0;
   if (tid < kH) mref[tid] = sink_ref(a.sink, tid);
@@ -263,7 +272,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
     const int buf = t % kBufs;
     const int jl = t * kT + wave * kCopyRows + (lane % kCopyRows);
     int code = -1;
-    if (jl < n_rows) code = HCA ? cand_code(a, true, c, qi, j_begin + jl) : codes[jl];
+    if (jl < n_rows) code = resolved ? codes[jl] : cand_code(a, true, c, qi, j_begin + jl);
     const uint64_t ok = __ballot(code != -1);
     if (lane == 0) vmask[buf][wave] = uint8_t(ok & ((1u << kCopyRows) - 1u));
     const uint32_t dst = lds_tiles + uint32_t(buf * kT * kPitch + wave * kCopyRows * kPitch);
@@ -1157,7 +1166,7 @@ __global__ __launch_bounds__(kWave) void attn_redo(AttnArgs a, const int* redo) 
 
 }  // namespace
 
-AttnPlan plan_attn(int B, int S, int H, int D, int window, int nsel, int dtype, bool hca) {
+AttnPlan plan_attn(int B, int S, int H, int D, int window, int nsel, int dtype, bool hca, bool paged) {
   AttnPlan p{false, false, 1, 0, 0};
   p.mfma = (dtype == CSA_BF16 || dtype == CSA_KV4) && H == kH && D == kD;
   if (!p.mfma) return p;
@@ -1171,7 +1180,7 @@ AttnPlan plan_attn(int B, int S, int H, int D, int window, int nsel, int dtype, 
   int64_t rows = (max_cand + want - 1) / want;
   rows = (rows + kSplitGrain - 1) / kSplitGrain * kSplitGrain;
   if (rows < kSplitGrain) rows = kSplitGrain;
-  if (!hca && rows > kMaxChunk) rows = kMaxChunk;
+  if ((!hca || paged) && rows > kMaxChunk) rows = kMaxChunk;  // chunks resolved into the code table
   p.chunk_rows = int(rows);
   p.nsplit = int((max_cand + rows - 1) / rows);
   if (p.nsplit < 1) p.nsplit = 1;
@@ -1181,8 +1190,8 @@ AttnPlan plan_attn(int B, int S, int H, int D, int window, int nsel, int dtype, 
   }
   if (p.nsplit > 1) {
     p.ws_bytes = size_t(nq) * p.nsplit * (size_t(kPartialVecs) * 16 + kH * 4 * sizeof(float));
-  } else if (nq >= kPersistMinQueries && (hca || nsel <= kPMaxSel) && dtype != CSA_KV4) {
-    // (quantised caches take one workgroup per query instead)
+  } else if (nq >= kPersistMinQueries && (hca || nsel <= kPMaxSel) && dtype != CSA_KV4 && !paged) {
+    // (quantised and paged caches take one workgroup per query instead)
     p.persist = true;
     p.ws_bytes = size_t(nq) * sizeof(int);  // per-query recompute flags
   }

@@ -60,23 +60,24 @@ __device__ __forceinline__ Task compress_task(const CompressArgs& a, int w) {
     if (w >= a.B * a.n_entries) return t;
     t.b = w / a.n_entries;
     t.e = a.e0 + w % a.n_entries;
-    t.live = true;
+    t.live = a.pt.pages == nullptr || paged_row(a.pt, t.b, t.e) >= 0;
   } else {
     if (w >= a.B) return t;
     const int p = a.pos[w];
     t.b = w;
     if (p < 0 || (p + 1) % a.ratio != 0) return t;
     t.e = p / a.ratio;
-    t.live = t.e < a.out_cap;
+    t.live = t.e < a.out_cap && (a.pt.pages == nullptr || paged_row(a.pt, t.b, t.e) >= 0);
   }
   return t;
 }
 
 // Quantised output: entry e of sequence b at out + b*out_bstride bytes + e
-// rows of kv4_row_bytes.
+// rows of kv4_row_bytes (contiguous), or its pool row (paged).
 __device__ __forceinline__ unsigned char* kv4_out_row(const CompressArgs& a, int b, int e) {
-  return static_cast<unsigned char*>(a.out) + int64_t(b) * a.out_bstride +
-         int64_t(e) * kv4_row_bytes(a.D, a.rope_dim);
+  const int rb = kv4_row_bytes(a.D, a.rope_dim);
+  if (a.pt.pages) return static_cast<unsigned char*>(a.out) + paged_row(a.pt, b, e) * rb;
+  return static_cast<unsigned char*>(a.out) + int64_t(b) * a.out_bstride + int64_t(e) * rb;
 }
 
 // Row of token `tok` inside a sequence's span (span mode) or ring (ring mode).
@@ -346,7 +347,7 @@ __global__ __launch_bounds__(kWave* max_waves(CPL)) void compress_lanes(Compress
   float tot = 0.f;
   for (int wv = 0; wv < nthr / kWave; ++wv) tot += red[wv];
   const float inv_rms = rsqrtf(tot / float(D) + a.eps);
-  const int64_t o = int64_t(task.b) * a.out_bstride + int64_t(e) * D;
+  const int64_t o = a.pt.pages ? paged_row(a.pt, task.b, e) * D : int64_t(task.b) * a.out_bstride + int64_t(e) * D;
 
   if (gr == 1) {
     // the lane's own channels, rotated in place (RoPE pairs never straddle
@@ -464,7 +465,7 @@ __global__ __launch_bounds__(kWave) void compress_any(CompressArgs a) {
     kv4_store_row(ybuf, D, a.rope_dim, kv4_out_row(a, task.b, e));
     return;
   }
-  const int64_t o = int64_t(task.b) * a.out_bstride + int64_t(e) * D;
+  const int64_t o = a.pt.pages ? paged_row(a.pt, task.b, e) * D : int64_t(task.b) * a.out_bstride + int64_t(e) * D;
   for (int c = lane; c < D; c += kWave) store_elem(a.out, a.out_dtype, o + c, ybuf[c]);
 }
 

@@ -76,16 +76,26 @@ __global__ __launch_bounds__(kWave* kStreamWaves) void index_stream(IndexArgs a)
       srow[e] = -INFINITY;
     return;
   }
-  const uint16_t* cache = static_cast<const uint16_t*>(a.cache) + int64_t(b) * Ncap * kDI;
+  const uint16_t* cache = static_cast<const uint16_t*>(a.cache) + (a.pt.pages ? 0 : int64_t(b) * Ncap * kDI);
   // per 16-row block and K-step, lane (g, r16) reads row r16, bytes ks*64 + g*16:
   // every load instruction covers 64 contiguous bytes of 16 rows
   auto load = [&](int step, uint4 (&kb)[4][4]) {
     const int64_t base = row0 + int64_t(step) * kStepRows + wave * 64;
+    // a paged cache: the wave's 64 rows share one page (pages hold a
+    // multiple of 64 rows); shift the base so that row e reads its pool row
+    const uint16_t* cb = cache;
+    if (a.pt.pages && base < n_vis) {
+      const int64_t lp = base >> a.pt.page_shift;
+      const int pg = a.pt.pages[int64_t(b) * a.pt.max_pages + lp];
+      // an unallocated or foreign page reads the pool's first page instead
+      // (its scores are still written; such a table is the caller's error)
+      cb = cache + ((int64_t(pg >= 0 && pg < a.pt.pool_pages ? pg : 0) - lp) << a.pt.page_shift) * kDI;
+    }
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
       const int64_t e = base + blk * 16 + r16;
       if (e < n_vis) {
-        const uint4* src = reinterpret_cast<const uint4*>(cache + e * kDI) + g;
+        const uint4* src = reinterpret_cast<const uint4*>(cb + e * kDI) + g;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) kb[blk][ks] = src[ks * 4];
       } else {
@@ -659,7 +669,9 @@ __global__ __launch_bounds__(256) void index_any(IndexArgs a) {
   const int64_t n_vis = visible_entries(a.pos, qi, a.ratio, a.Ncap);
   float* srow = a.scores + qi * a.Ncap;
   if (e >= n_vis) { srow[e] = -INFINITY; return; }
-  const int64_t row = (int64_t(b) * a.Ncap + e) * D;
+  const int64_t prow = a.pt.pages ? paged_row(a.pt, b, e) : int64_t(b) * a.Ncap + e;
+  if (prow < 0) { srow[e] = -INFINITY; return; }  // a paged entry without a page of the pool
+  const int64_t row = prow * D;
   float sc = 0.f;
   for (int h = 0; h < H; ++h) {
     float dot = 0.f;
@@ -688,15 +700,17 @@ int cu_count() {
 hipError_t launch_index_score(const IndexArgs& a, hipStream_t stream) {
   const int64_t nq = int64_t(a.B) * a.S;
   if (nq == 0 || a.Ncap == 0) return hipSuccess;
-  if (a.use_mfma && a.H == kHI && a.D == kDI && a.S >= 2 * kTQ && a.Ncap % 4 == 0) {
+  const bool paged = a.pt.pages != nullptr;  // paged caches: the streaming kernel or the vector path
+  if (!paged && a.use_mfma && a.H == kHI && a.D == kDI && a.S >= 2 * kTQ && a.Ncap % 4 == 0) {
     const int gps = (a.S + kTQ - 1) / kTQ;
     const int ngroups = a.B * gps;
     hipLaunchKernelGGL(index_tile, dim3(unsigned(ngroups)), dim3(kTThreads), 0, stream, a, gps, ngroups);
-  } else if (a.use_mfma && a.H == kHI && a.D == kDI && a.Ncap % 4 == 0 && nq <= kFlatMaxQ &&
+  } else if (!paged && a.use_mfma && a.H == kHI && a.D == kDI && a.Ncap % 4 == 0 && nq <= kFlatMaxQ &&
              nq * int64_t(a.Ncap) >= (int64_t(1) << 21)) {
     // long caches (>= 2M rows in all): balanced persistent streaming
     hipLaunchKernelGGL(index_flat, dim3(unsigned(cu_count())), dim3(kDW * kWave), 0, stream, a);
-  } else if (a.use_mfma && a.H == kHI && a.D == kDI && a.Ncap % 4 == 0 && nq * int64_t(a.Ncap) >= (int64_t(1) << 21)) {
+  } else if (!paged && a.use_mfma && a.H == kHI && a.D == kDI && a.Ncap % 4 == 0 &&
+             nq * int64_t(a.Ncap) >= (int64_t(1) << 21)) {
     // long caches of more queries than index_flat's prefix holds: rows per
     // wave the smallest of 32 .. 512 that keeps the grid within 2048 workgroups
     const int64_t rows = nq * int64_t(a.Ncap);

@@ -7,6 +7,22 @@
 
 namespace csa {
 
+// A paged cache: entry e of sequence b lives in pool row
+// (pages[b*max_pages + (e >> page_shift)] << page_shift) + (e & (page_rows-1));
+// pages == nullptr means the contiguous layout.
+struct PageTable {
+  const int* pages;
+  int max_pages;
+  int page_shift;
+  int pool_pages;  // pages in the pool: table entries outside [0, pool_pages) are skipped
+};
+// Pool row of entry e of sequence b (-1 when its page is not allocated or
+// not a page of the pool).
+__device__ __forceinline__ int64_t paged_row(const PageTable& pt, int b, int64_t e) {
+  const int pg = pt.pages[int64_t(b) * pt.max_pages + (e >> pt.page_shift)];
+  return (pg < 0 || pg >= pt.pool_pages) ? -1 : (int64_t(pg) << pt.page_shift) + (e & ((int64_t(1) << pt.page_shift) - 1));
+}
+
 struct CompressArgs {
   const void* kv;
   const void* gate;
@@ -26,6 +42,7 @@ struct CompressArgs {
   int64_t out_bstride;
   int out_cap;
   void* ws;  // split partials and counters (zero counters on entry, left zero)
+  PageTable pt;  // paged output (out is then the pool)
 };
 // Compressor plan, shared by the workspace-size query and the launch.
 struct CompressPlan {
@@ -49,6 +66,7 @@ struct IndexArgs {
   int B, S, H, D, Ncap, ratio;
   float* scores;
   bool use_mfma;  // bf16, 64 heads x 128, 16-byte aligned operands
+  PageTable pt;   // paged index cache (cache is then the pool)
 };
 hipError_t launch_index_score(const IndexArgs& a, hipStream_t stream);
 
@@ -87,6 +105,7 @@ struct AttnArgs {
   void* ws;
   int cmp_q4;         // cmp rows are quantised (kv4.h); q and win are then bf16
   int cmp_row_bytes;  // bytes per quantised cmp row
+  PageTable pt;       // paged compressed cache (cmp is then the pool)
 };
 struct AttnPlan {
   bool mfma;
@@ -95,7 +114,7 @@ struct AttnPlan {
   int chunk_rows;
   size_t ws_bytes;
 };
-AttnPlan plan_attn(int B, int S, int H, int D, int window, int nsel, int dtype, bool hca);
+AttnPlan plan_attn(int B, int S, int H, int D, int window, int nsel, int dtype, bool hca, bool paged = false);
 hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, bool hca, hipStream_t stream);
 
 // Quantisation of rows into the FP4/FP8 cache format of kv4.h.

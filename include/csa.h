@@ -59,7 +59,8 @@ enum {
   CSA_ERR_INVALID_ARG = -1,   /* null pointer, bad size, inconsistent shapes   */
   CSA_ERR_UNSUPPORTED = -2,   /* shape / dtype combination not compiled        */
   CSA_ERR_HIP = -3,           /* a HIP launch or runtime call failed           */
-  CSA_ERR_WORKSPACE = -4      /* ws_bytes below the matching *_workspace_size  */
+  CSA_ERR_WORKSPACE = -4,     /* ws_bytes below the matching *_workspace_size  */
+  CSA_ERR_NO_PAGES = -5       /* a page pool has too few free pages            */
 };
 
 /* Static, human-readable name of a status code. */
@@ -315,6 +316,87 @@ int hca_attn(const void* q, const void* cmp, int Ncap, int ratio,
              int dtype, float scale, int rope_dim, float rope_base,
              int B, int S, int H, int D, void* out, int out_dtype,
              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Paged, variable-length compressed caches.
+ *
+ * [LLM Atlas] §19 "V4 / HETEROGENEOUS STATE MACHINE": real serving depends on
+ * the batch, the distribution of sequence lengths, quantisation and the page
+ * allocator.  A paged cache keeps the rows of all sequences in one pool of
+ * pages of page_rows rows each (rows as in the contiguous layout: D elements
+ * of the cache dtype, or csa_kv4_row_bytes bytes); a block table maps
+ * logical page j of sequence b to a pool page:
+ *   entry e of sequence b -> pool row pages[b*max_pages + e/page_rows]*page_rows
+ *                                      + e % page_rows
+ * so sequences grow page by page, independently of each other.
+ *
+ *   pages       DEVICE int32 [B, max_pages]; -1 marks a page not allocated.
+ *               Entries the kernels reach must be pool pages in
+ *               [0, pool_pages) (others are skipped: an appended entry is not
+ *               written, an attended row is left out, an index score is -inf
+ *               on the vector path).
+ *   page_rows   a power of two >= 64 (the indexer's waves read 64 rows at a time).
+ *   pool_pages  pages in the pool.
+ * The logical capacity of a sequence is Ncap = max_pages * page_rows; score
+ * rows stay [B, S, Ncap] in logical order and top-k is unchanged.
+ */
+typedef struct csa_page_table {
+  const int* pages;
+  int max_pages;
+  int page_rows;
+  int pool_pages;
+} csa_page_table;
+
+/* csa_compress with its output in a paged cache: `job` holds the arguments
+ * of one csa_compress call with out = the pool (out_bstride and out_cap are
+ * taken from the table).  Ring mode appends entry pos/r of sequence b at its
+ * pool row; span mode writes entries e0 .. e0+n-1. */
+int csa_compress_paged(const csa_compress_job* job, const csa_page_table* out_pages, hipStream_t stream);
+
+/* csa_index_score over a paged index-key cache (idx_pool: the pool; Ncap =
+ * max_pages*page_rows).  Matrix-core shapes take the streaming kernel. */
+int csa_index_score_paged(const void* q_idx, const float* w, const void* idx_pool, int dtype, const int* pos,
+                          int B, int S, int H_I, int D_I, const csa_page_table* pages, int ratio, float* scores,
+                          hipStream_t stream);
+
+/* csa_sparse_attn / hca_attn over a paged compressed cache (cmp_pool: the
+ * pool, bf16 rows or, with dtype CSA_KV4, quantised rows).  Selections are
+ * logical entries.  Workspace: csa_sparse_attn_workspace_size /
+ * hca_attn_workspace_size (with Ncap = max_pages*page_rows) cover the paged
+ * plans. */
+int csa_sparse_attn_paged(const void* q, const void* cmp_pool, const csa_page_table* pages, const int* idx, int k,
+                          const void* win, int Wcap, int window, const int* pos, const float* sink, int dtype,
+                          float scale, int rope_dim, float rope_base, int B, int S, int H, int D, void* out,
+                          int out_dtype, void* ws, size_t ws_bytes, hipStream_t stream);
+int hca_attn_paged(const void* q, const void* cmp_pool, const csa_page_table* pages, int ratio, const void* win,
+                   int Wcap, int window, const int* pos, const float* sink, int dtype, float scale, int rope_dim,
+                   float rope_base, int B, int S, int H, int D, void* out, int out_dtype, void* ws,
+                   size_t ws_bytes, hipStream_t stream);
+
+/*
+ * csa_page_pool -- the page allocator behind paged caches (host memory only;
+ * the device pool itself is the caller's allocation).
+ *
+ * create: a pool of n_pages free pages (NULL when n_pages < 1 or out of
+ *   host memory); pages are handed out lowest-numbered first while the pool
+ *   is fresh, then most recently released first.
+ * alloc: n pages into the HOST array pages, or CSA_ERR_NO_PAGES (nothing
+ *   taken).  release: gives n pages back; every page must be in use and
+ *   named once, else CSA_ERR_INVALID_ARG and nothing is released.
+ * csa_page_table_reserve: makes a sequence's HOST table row (max_pages
+ *   entries, -1 = none) cover n_entries entries, allocating only the missing
+ *   pages (all or nothing).  csa_page_table_release frees every page of a row
+ *   and sets it to -1.  Upload the table to the device before the kernels
+ *   read it.  All calls are thread-safe.
+ */
+typedef struct csa_page_pool csa_page_pool;
+csa_page_pool* csa_page_pool_create(int n_pages);
+void csa_page_pool_destroy(csa_page_pool* pool);
+int csa_page_pool_available(csa_page_pool* pool);
+int csa_page_pool_alloc(csa_page_pool* pool, int n, int* pages);
+int csa_page_pool_release(csa_page_pool* pool, int n, const int* pages);
+int csa_page_table_reserve(csa_page_pool* pool, int* row, int max_pages, int page_rows, int64_t n_entries);
+int csa_page_table_release(csa_page_pool* pool, int* row, int max_pages);
 
 /*
  * csa_q_proj -- the low-rank query path in front of the attention.

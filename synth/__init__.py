@@ -51,6 +51,7 @@ class Config:
     rope_base: float = 10000.0
     dtype: str = "bf16"
     kv4: bool = False    # compressed KV cache stored quantised (FP4 latent, FP8 RoPE tail)
+    page_rows: int = 0   # decode: caches held in a shared page pool of pages of this many rows (0: contiguous)
 
 
 TINY = Config("tiny_csa", 0, "tiny", B=1, H=2, D=32, rope_dim=8, H_I=2, D_I=16,
@@ -75,9 +76,15 @@ ATTN_BLOCK_DECODE_64K = Config("attn_block_decode_64k", 6, "block", B=8, ctx=655
 CSA_DECODE_64K_KV4 = Config("csa_decode_64k_kv4", 7, "decode", B=8, ctx=65536, kv4=True)
 HCA_DECODE_1M_KV4 = Config("hca_decode_1m_kv4", 8, "decode", B=4, ctx=1048576, ratio=128, overlap=0, csa=False,
                            kv4=True)
+# the long-context decode with its length mix served from paged caches ("LLM
+# Atlas: DeepSeek", section 19: serving cost depends on the sequence-length mix
+# and the allocator): the same seeded draw as csa_decode_1m (same stream id),
+# its rows in one shared pool of 256-row pages handed out by the page allocator
+CSA_DECODE_1M_PAGED = Config("csa_decode_1m_paged", 4, "decode", B=32, ctx=1048576, ctx_lo=524288, page_rows=256)
 
 CONFIGS = {c.name: c for c in (TINY, CSA_DECODE_64K, HCA_DECODE_1M, CSA_PREFILL_8K, CSA_DECODE_1M,
-                               CSA_DECODE_64K_K1024, ATTN_BLOCK_DECODE_64K, CSA_DECODE_64K_KV4, HCA_DECODE_1M_KV4)}
+                               CSA_DECODE_64K_K1024, ATTN_BLOCK_DECODE_64K, CSA_DECODE_64K_KV4, HCA_DECODE_1M_KV4,
+                               CSA_DECODE_1M_PAGED)}
 
 # tensor ids of the seeded streams
 T_X, T_WKV, T_WG, T_WKI, T_WGI, T_WQ, T_WQI, T_WW = 0, 1, 2, 3, 4, 5, 6, 7
