@@ -400,7 +400,7 @@ class PagedDecodeWorkload(DecodeWorkload):
                        pages=self.table, page_rows=pr, ratio=cfg.ratio, overlap=cfg.overlap,
                        rope_dim=cfg.rope_dim_idx, rope_base=cfg.rope_base, eps=cfg.eps, pos=self.pos, ws=self.ws_cidx)
         return [
-            ("compress", lambda: (csa.csa_compress_paged(**kv_job), csa.csa_compress_paged(**idx_job))),
+            ("compress", lambda: csa.csa_compress_paged_jobs([kv_job, idx_job])),
             ("index_score", lambda: csa.csa_index_score_paged(self.q_idx, self.w, self.idx_cache[c], self.pos2,
                                                               self.scores, self.table, page_rows=pr,
                                                               ratio=cfg.ratio)),

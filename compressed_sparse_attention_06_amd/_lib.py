@@ -51,7 +51,7 @@ SIGNATURES = {
                               _c_int, _c_f, _c_f, _c_int, _c_int, _c_int, _c_p, _c_p, _c_int, _c_i64, _c_int, _c_p,
                               _c_sz, _c_p]),
     "csa_compress_jobs": (_c_int, [ctypes.POINTER(CompressJob), _c_int, _c_p]),
-    "csa_compress_paged": (_c_int, [ctypes.POINTER(CompressJob), ctypes.POINTER(PageTableC), _c_p]),
+    "csa_compress_paged": (_c_int, [ctypes.POINTER(CompressJob), ctypes.POINTER(PageTableC), _c_int, _c_p]),
     "csa_index_score_paged": (_c_int, [_c_p, _c_p, _c_p, _c_int, _c_p, _c_int, _c_int, _c_int, _c_int,
                                        ctypes.POINTER(PageTableC), _c_int, _c_p, _c_p]),
     "csa_sparse_attn_paged": (_c_int, [_c_p, _c_p, ctypes.POINTER(PageTableC), _c_p, _c_int, _c_p, _c_int, _c_int,
@@ -354,13 +354,14 @@ def _page_table(pages, page_rows, pool):
     return PageTableC(_ptr(pages), pages.shape[1], page_rows, pool.shape[0] // page_rows)
 
 
-def csa_compress_paged(kv, gate, gamma, pool, pages, *, page_rows, ratio, overlap, rope_dim, rope_base=10000.0,
-                       eps=1e-6, kv_prev=None, gate_prev=None, tok0=0, e0=0, n_entries=None, pos=None, ws=None,
-                       stream=None):
-    """csa_compress into a paged cache: pool [pool_rows, D] (or uint8 [pool_rows, row_bytes] quantised),
-    pages [B, max_pages] int32.  Span mode needs n_entries."""
+def _paged_job(kv, gate, gamma, pool, pages, *, page_rows, ratio, overlap, rope_dim, rope_base=10000.0, eps=1e-6,
+               kv_prev=None, gate_prev=None, tok0=0, e0=0, n_entries=None, pos=None, ws=None):
+    """(CompressJob, csa_page_table, tensors they point to) for one paged compressor call."""
     B, T, D = kv.shape
     bstride = _rows(kv)
+    for t in (gate, kv_prev, gate_prev):
+        if t is not None and (t.shape != kv.shape or _rows(t) != bstride):
+            raise CsaError("kv, gate, kv_prev and gate_prev must share one layout")
     _dense(gamma, pos, pool)
     if pos is None and n_entries is None:
         raise CsaError("span mode needs n_entries")
@@ -371,10 +372,31 @@ def csa_compress_paged(kv, gate, gamma, pool, pages, *, page_rows, ratio, overla
     job = CompressJob(_ptr(kv), _ptr(gate), _ptr(kv_prev), _ptr(gate_prev), _dtype(kv), _ptr(gamma), B, T, bstride,
                       D, ratio, overlap, rope_dim, rope_base, eps, tok0, e0, n, _ptr(pos), _ptr(pool), _dtype(pool),
                       0, 0, _ptr(ws), _bytes(ws))
-    pt = _page_table(pages, page_rows, pool)
-    st = lib().csa_compress_paged(ctypes.byref(job), ctypes.byref(pt), _stream(stream))
-    _check(st, "csa_compress_paged")
+    return job, _page_table(pages, page_rows, pool), (kv, gate, gamma, pool, pages, kv_prev, gate_prev, pos, ws)
+
+
+def csa_compress_paged(kv, gate, gamma, pool, pages, *, page_rows, ratio, overlap, rope_dim, rope_base=10000.0,
+                       eps=1e-6, kv_prev=None, gate_prev=None, tok0=0, e0=0, n_entries=None, pos=None, ws=None,
+                       stream=None):
+    """csa_compress into a paged cache: pool [pool_rows, D] (or uint8 [pool_rows, row_bytes] quantised),
+    pages [B, max_pages] int32.  Span mode needs n_entries."""
+    csa_compress_paged_jobs([dict(kv=kv, gate=gate, gamma=gamma, pool=pool, pages=pages, page_rows=page_rows,
+                                  ratio=ratio, overlap=overlap, rope_dim=rope_dim, rope_base=rope_base, eps=eps,
+                                  kv_prev=kv_prev, gate_prev=gate_prev, tok0=tok0, e0=e0, n_entries=n_entries,
+                                  pos=pos, ws=ws)], stream=stream)
     return pool
+
+
+def csa_compress_paged_jobs(jobs, stream=None):
+    """Paged compressor calls in one launch: `jobs` is a list of dicts holding the keyword arguments of
+    csa_compress_paged (kv, gate, gamma, pool, pages, page_rows, ratio, ...)."""
+    built = [_paged_job(**j) for j in jobs]
+    n = max(1, len(built))
+    arr = (CompressJob * n)(*[b[0] for b in built])
+    tabs = (PageTableC * n)(*[b[1] for b in built])
+    st = lib().csa_compress_paged(arr, tabs, len(built), _stream(stream))
+    _check(st, "csa_compress_paged")
+    return [j["pool"] for j in jobs]
 
 
 def csa_index_score_paged(q_idx, w, idx_pool, pos, scores, pages, *, page_rows, ratio, stream=None):

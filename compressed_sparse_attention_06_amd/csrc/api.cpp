@@ -161,18 +161,21 @@ int csa_compress(const void* kv, const void* gate, const void* kv_prev, const vo
   return hip_status(csa::launch_compress(&a, &plan, 1, stream));
 }
 
-int csa_compress_paged(const csa_compress_job* job, const csa_page_table* out_pages, hipStream_t stream) {
-  if (job == nullptr) return CSA_ERR_INVALID_ARG;
-  csa::PageTable pt;
-  int st = page_table(out_pages, &pt);
-  if (st != CSA_OK) return st;
-  csa_compress_job j = *job;
-  j.out_cap = out_pages->max_pages * out_pages->page_rows;  // the logical capacity of a sequence
-  csa::CompressArgs a;
-  csa::CompressPlan plan;
-  st = compress_job(j, &a, &plan, &pt);
-  if (st != CSA_OK) return st;
-  return hip_status(csa::launch_compress(&a, &plan, 1, stream));
+int csa_compress_paged(const csa_compress_job* jobs, const csa_page_table* tables, int n_jobs, hipStream_t stream) {
+  if (n_jobs < 0 || n_jobs > CSA_MAX_COMPRESS_JOBS || (n_jobs > 0 && (jobs == nullptr || tables == nullptr)))
+    return CSA_ERR_INVALID_ARG;
+  csa::CompressArgs a[CSA_MAX_COMPRESS_JOBS];
+  csa::CompressPlan plan[CSA_MAX_COMPRESS_JOBS];
+  for (int i = 0; i < n_jobs; ++i) {
+    csa::PageTable pt;
+    int st = page_table(&tables[i], &pt);
+    if (st != CSA_OK) return st;
+    csa_compress_job j = jobs[i];
+    j.out_cap = tables[i].max_pages * tables[i].page_rows;  // the logical capacity of a sequence
+    st = compress_job(j, &a[i], &plan[i], &pt);
+    if (st != CSA_OK) return st;
+  }
+  return hip_status(csa::launch_compress(a, plan, n_jobs, stream));
 }
 
 int csa_compress_jobs(const csa_compress_job* jobs, int n_jobs, hipStream_t stream) {

@@ -436,6 +436,10 @@ __global__ __launch_bounds__(kDW * kWave) void index_dma(IndexArgs a) {
 // operands when its range enters that query, and sends its scores out in one
 // 1 KiB store per 256 rows.  Afterwards the workgroups share the -inf fill of
 // every row past a query's last chunk.
+// PAGED: the rows live in a page pool (pages of a power-of-two multiple of 64
+// rows, so a 16-row chunk never straddles two); the issuing cursor keeps the
+// pool page of its current logical page and, on entering a page, requests
+// the next one's table entry, which arrives long before the cursor needs it.
 // ---------------------------------------------------------------------------
 constexpr int kFlatMaxQ = 1024;  // queries whose chunk counts fit in LDS
 constexpr int kFlush = 256;      // score rows per store
@@ -462,6 +466,7 @@ __device__ __forceinline__ void wait_vmem_upto15(int n) {
   }
 }
 
+template <bool PAGED>
 __global__ __launch_bounds__(kDW * kWave) void index_flat(IndexArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char ring[kDW][kDSlots][kDChunk * kRowB];
   __shared__ __attribute__((aligned(16))) float sc[kDW][kFlush];
@@ -525,9 +530,15 @@ __global__ __launch_bounds__(kDW * kWave) void index_flat(IndexArgs a) {
   };
   struct Cur {
     int q, lc, nch, nv;  // query, its chunk, its chunk count, its visible rows
+    int pq, plp, pg;     // (PAGED, issuing cursor) query and logical page of pool page pg
+    int pnext;           // its table entry for logical page plp + 1 (requested, maybe in flight)
   };
   auto at = [&](int64_t c) -> Cur {
     Cur u;
+    u.pq = -1;
+    u.plp = -1;
+    u.pg = 0;
+    u.pnext = 0;
     u.q = __builtin_amdgcn_readfirstlane(find(cpre, c));
     u.lc = __builtin_amdgcn_readfirstlane(int(c - cpre[u.q]));
     u.nch = __builtin_amdgcn_readfirstlane(int(cpre[u.q + 1] - cpre[u.q]));
@@ -553,12 +564,37 @@ __global__ __launch_bounds__(kDW * kWave) void index_flat(IndexArgs a) {
   const uint32_t ring_base = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)&ring[wave][0][0]));
   // chunk u into ring slot `slot`: 4 copies of 4 rows; rows past the causal
   // bound repeat the last visible row (finite, masked)
-  auto issue = [&](const Cur& u, int slot) {
-    const uint16_t* cache = cache0 + int64_t(u.q / a.S) * Ncap * kDI;
+  // a table entry as a pool page; an unallocated or foreign page reads the
+  // pool's first page instead (its scores are still written; such a table is
+  // the caller's error)
+  auto pool_page = [&](int pg) { return (pg >= 0 && pg < a.pt.pool_pages) ? pg : 0; };
+  // (read through the constant address space: a scalar load, whose wait
+  // leaves the ring copies in flight)
+  auto table_entry = [&](int q, int lp) {
+    const __attribute__((address_space(4))) int* t = (const __attribute__((address_space(4))) int*)a.pt.pages;
+    return t[int64_t(q / a.S) * a.pt.max_pages + lp];
+  };
+  auto issue = [&](Cur& u, int slot) {
+    const uint16_t* cache;
+    int e_base = 0;  // first row of `cache`, in the query's entry numbering
+    if constexpr (PAGED) {
+      const int lp = (u.lc * kDChunk) >> a.pt.page_shift;
+      if (u.q != u.pq || lp != u.plp) {
+        const int pg = (u.q == u.pq && lp == u.plp + 1) ? u.pnext : table_entry(u.q, lp);
+        u.pg = __builtin_amdgcn_readfirstlane(pool_page(pg));
+        u.pq = u.q;
+        u.plp = lp;
+        if (int64_t(lp + 1) << a.pt.page_shift < u.nv) u.pnext = table_entry(u.q, lp + 1);
+      }
+      cache = cache0 + (int64_t(u.pg) << a.pt.page_shift) * kDI;
+      e_base = lp << a.pt.page_shift;
+    } else {
+      cache = cache0 + int64_t(u.q / a.S) * Ncap * kDI;
+    }
 #pragma unroll
     for (int cp = 0; cp < kDCopies; ++cp) {
       const int rl = cp * 4 + g;
-      const int e = min(u.lc * kDChunk + rl, u.nv - 1);
+      const int e = min(u.lc * kDChunk + rl, u.nv - 1) - e_base;
       const uint32_t voff = uint32_t(e) * kRowB + uint32_t(((r16 ^ (rl & 15)) << 4));
       copy_to_lds(cache, voff, ring_base + uint32_t(slot * kDChunk * kRowB + cp * 4 * kRowB));
     }
@@ -700,15 +736,16 @@ int cu_count() {
 hipError_t launch_index_score(const IndexArgs& a, hipStream_t stream) {
   const int64_t nq = int64_t(a.B) * a.S;
   if (nq == 0 || a.Ncap == 0) return hipSuccess;
-  const bool paged = a.pt.pages != nullptr;  // paged caches: the streaming kernel or the vector path
+  const bool paged = a.pt.pages != nullptr;  // paged caches: the streaming kernels or the vector path
   if (!paged && a.use_mfma && a.H == kHI && a.D == kDI && a.S >= 2 * kTQ && a.Ncap % 4 == 0) {
     const int gps = (a.S + kTQ - 1) / kTQ;
     const int ngroups = a.B * gps;
     hipLaunchKernelGGL(index_tile, dim3(unsigned(ngroups)), dim3(kTThreads), 0, stream, a, gps, ngroups);
-  } else if (!paged && a.use_mfma && a.H == kHI && a.D == kDI && a.Ncap % 4 == 0 && nq <= kFlatMaxQ &&
+  } else if (a.use_mfma && a.H == kHI && a.D == kDI && a.Ncap % 4 == 0 && nq <= kFlatMaxQ &&
              nq * int64_t(a.Ncap) >= (int64_t(1) << 21)) {
     // long caches (>= 2M rows in all): balanced persistent streaming
-    hipLaunchKernelGGL(index_flat, dim3(unsigned(cu_count())), dim3(kDW * kWave), 0, stream, a);
+    if (paged) hipLaunchKernelGGL(index_flat<true>, dim3(unsigned(cu_count())), dim3(kDW * kWave), 0, stream, a);
+    else hipLaunchKernelGGL(index_flat<false>, dim3(unsigned(cu_count())), dim3(kDW * kWave), 0, stream, a);
   } else if (!paged && a.use_mfma && a.H == kHI && a.D == kDI && a.Ncap % 4 == 0 &&
              nq * int64_t(a.Ncap) >= (int64_t(1) << 21)) {
     // long caches of more queries than index_flat's prefix holds: rows per

@@ -332,9 +332,11 @@ int hca_attn(const void* q, const void* cmp, int Ncap, int ratio,
  *
  *   pages       DEVICE int32 [B, max_pages]; -1 marks a page not allocated.
  *               Entries the kernels reach must be pool pages in
- *               [0, pool_pages) (others are skipped: an appended entry is not
- *               written, an attended row is left out, an index score is -inf
- *               on the vector path).
+ *               [0, pool_pages).  Others are the caller's error and never
+ *               leave the pool: an appended entry is not written, an attended
+ *               row is left out, and an index score is -inf on the vector
+ *               path but, on the matrix-core kernels, the score of the pool's
+ *               first page's row (finite, meaningless).
  *   page_rows   a power of two >= 64 (the indexer's waves read 64 rows at a time).
  *   pool_pages  pages in the pool.
  * The logical capacity of a sequence is Ncap = max_pages * page_rows; score
@@ -347,11 +349,13 @@ typedef struct csa_page_table {
   int pool_pages;
 } csa_page_table;
 
-/* csa_compress with its output in a paged cache: `job` holds the arguments
- * of one csa_compress call with out = the pool (out_bstride and out_cap are
- * taken from the table).  Ring mode appends entry pos/r of sequence b at its
- * pool row; span mode writes entries e0 .. e0+n-1. */
-int csa_compress_paged(const csa_compress_job* job, const csa_page_table* out_pages, hipStream_t stream);
+/* csa_compress_jobs with outputs in paged caches: jobs[i] holds the
+ * arguments of one csa_compress call with out = its pool (out_bstride and
+ * out_cap are taken from tables[i]), and all n_jobs (0 .. CSA_MAX_COMPRESS_JOBS)
+ * run in one launch, e.g. the KV and index-key appends of a decode step.
+ * Ring mode appends entry pos/r of sequence b at its pool row; span mode
+ * writes entries e0 .. e0+n-1.  Host arrays, read before the call returns. */
+int csa_compress_paged(const csa_compress_job* jobs, const csa_page_table* tables, int n_jobs, hipStream_t stream);
 
 /* csa_index_score over a paged index-key cache (idx_pool: the pool; Ncap =
  * max_pages*page_rows).  Matrix-core shapes take the streaming kernel. */

@@ -54,9 +54,9 @@ def _paginate(cache, rows_used, page_rows, seed, spare_pages=5):
     else:
         pool = torch.full((n_pool * page_rows, W), 1000.0, dtype=cache.dtype, device="cuda")
     for b in range(B):
-        for j in range(need[b]):
-            pg = int(table[b, j])
-            pool[pg * page_rows:(pg + 1) * page_rows] = cache[b, j * page_rows:(j + 1) * page_rows]
+        rows = min(need[b] * page_rows, Ncap)
+        dst = (torch.from_numpy(table[b, :need[b]]).long()[:, None] * page_rows + torch.arange(page_rows)).view(-1)
+        pool[dst[:rows].cuda()] = cache[b, :rows]
     return pool, dev(table), table
 
 
@@ -64,16 +64,22 @@ def _bits(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
 
 
-@pytest.mark.parametrize("page_rows", [256, 64])
-def test_paged_index_scores_match_contiguous(page_rows):
+@pytest.mark.parametrize("page_rows,long", [(256, False), (64, False), (128, True)])
+def test_paged_index_scores_match_contiguous(page_rows, long):
+    """Short caches take the streaming kernel, long ones (2M rows and more in
+    all) the balanced persistent one, paged or not."""
     import compressed_sparse_attention_06_amd as csa
-    B, Ncap = 4, 4096
+    B, Ncap = (4, 1 << 20) if long else (4, 4096)
     rng = np.random.default_rng(1)
-    vis = np.array([4096, 1000, 300, 2049])
+    vis = np.array([Ncap, 1000, 300, 2049]) if not long else np.array([Ncap, 700_001, 17, 262_144])
     pos = dev((4 * vis - 1).astype(np.int32)[:, None])
     qi = dev_bf16(synth.bf16_bits(synth.unit_rms(rng, (B, 1, 64, 128))))
     w = dev((rng.standard_normal((B, 1, 64)) / 128 ** 0.5 / 8).astype(np.float32))
-    cache = dev_bf16(synth.bf16_bits(synth.unit_rms(rng, (B, Ncap, 128))))
+    if long:  # (512 MiB of rows: drawn on the device from a seeded generator)
+        gen = torch.Generator(device="cuda").manual_seed(1)
+        cache = torch.randn((B, Ncap, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    else:
+        cache = dev_bf16(synth.bf16_bits(synth.unit_rms(rng, (B, Ncap, 128))))
     want = torch.empty((B, 1, Ncap), device="cuda")
     csa.csa_index_score(qi, w, cache, pos, want, ratio=4)
     pool, table, _ = _paginate(cache, vis, page_rows, 2)
@@ -81,12 +87,13 @@ def test_paged_index_scores_match_contiguous(page_rows):
     csa.csa_index_score_paged(qi, w, pool, pos, got, table, page_rows=page_rows, ratio=4)
     torch.cuda.synchronize()
     assert torch.equal(got, want)
-    # and the oracle on one sequence
+    # and the oracle on the first and last visible rows of one sequence
     b = 1
-    o = oracle.index_score(host(qi)[b, 0], host(w)[b, 0], host(cache)[b], int(vis[b]))
-    g = got.cpu().numpy()[b, 0]
+    rows = np.r_[0:min(2048, vis[b]), max(vis[b] - 2048, 0):vis[b]]
+    o = oracle.index_score(host(qi)[b, 0], host(w)[b, 0], host(cache[b, torch.from_numpy(rows).cuda()]), len(rows))
+    g = got[b, 0].cpu().numpy()
     assert np.all(np.isneginf(g[vis[b]:]))
-    assert np.max(np.abs(g[:vis[b]] - o[:vis[b]])) <= 1e-3 * np.max(np.abs(o[:vis[b]]))
+    assert np.max(np.abs(g[rows] - o)) <= 1e-3 * np.max(np.abs(o))
 
 
 def _attn_inputs(seed, B, S, Ncap, kv4, window=128, Wcap=128):
@@ -298,10 +305,10 @@ def test_paged_decode_steps_with_the_page_pool():
         outs = []
         for paged in (False, True):
             if paged:
-                csa.csa_compress_paged(stg[0], stg[1], gamma, kv_pool, table, page_rows=page_rows, ratio=r, overlap=1,
-                                       rope_dim=64, pos=pos)
-                csa.csa_compress_paged(stg[2], stg[3], gamma_i, ix_pool, table, page_rows=page_rows, ratio=r,
-                                       overlap=1, rope_dim=64, pos=pos)
+                # both appends in one launch
+                common = dict(pages=table, page_rows=page_rows, ratio=r, overlap=1, rope_dim=64, pos=pos)
+                csa.csa_compress_paged_jobs([dict(kv=stg[0], gate=stg[1], gamma=gamma, pool=kv_pool, **common),
+                                             dict(kv=stg[2], gate=stg[3], gamma=gamma_i, pool=ix_pool, **common)])
             else:
                 csa.csa_compress(stg[0], stg[1], gamma, kv_c, ratio=r, overlap=1, rope_dim=64, pos=pos)
                 csa.csa_compress(stg[2], stg[3], gamma_i, ix_c, ratio=r, overlap=1, rope_dim=64, pos=pos)

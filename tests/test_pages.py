@@ -117,6 +117,12 @@ def test_paged_entry_points_reject_bad_tables(lib, bad):
                               P, 1 << 30, None) == INVALID
     job = CompressJob(P, P, None, None, 1, P, 2, 8, 8 * 512, 512, 4, 1, 64, 1e4, 1e-6, 0, 0, 0, P, P, 1, 0, 0,
                       None, 0)
-    assert lib.csa_compress_paged(ctypes.byref(job), ctypes.byref(pt), None) == INVALID
-    assert lib.csa_compress_paged(None, ctypes.byref(_pt()), None) == INVALID
+    assert lib.csa_compress_paged(ctypes.byref(job), ctypes.byref(pt), 1, None) == INVALID
+    # a bad table behind a good one in the same launch
+    jobs = (CompressJob * 2)(job, job)
+    tabs = (PageTableC * 2)(_pt(), pt)
+    assert lib.csa_compress_paged(jobs, tabs, 2, None) == INVALID
+    assert lib.csa_compress_paged(None, ctypes.byref(_pt()), 1, None) == INVALID
+    assert lib.csa_compress_paged(ctypes.byref(job), None, 1, None) == INVALID
+    assert lib.csa_compress_paged(jobs, tabs, 17, None) == INVALID   # more than CSA_MAX_COMPRESS_JOBS
     assert lib.csa_index_score_paged(P, P, P, 1, P, 2, 1, 64, 128, None, 4, P, None) == INVALID
