@@ -11,13 +11,15 @@
 // At decode the token count M is small and each projection streams its
 // weight matrix from HBM once: ~8 flop per weight byte at M = 8, far under
 // the matrix cores' ridge, so the kernel is built to keep HBM busy.  A block
-// owns 16 output rows (weight rows) and all M tokens; its 8 waves split the
-// K axis and meet in LDS.  Each lane reads 64 contiguous bytes of a weight
-// row per 128-wide K block (16 rows x 256 B per wave), which the matrix core
-// consumes as four 16x16x32 bf16 products whose K chunks are permuted the
-// same way on both operands.  Activations are tiny and L2-resident; an fp32
-// activation is split into a bf16 head and a bf16 remainder (two products),
-// so the contraction keeps ~16 mantissa bits of it.
+// owns 128 output rows (weight rows; a 16-row tile per wave), one K chunk
+// and up to 32 tokens; the K chunks of one row tile run in different blocks
+// (enough blocks to spread the weights over the chip) and leave fp32
+// partials that the next step sums.  Each lane reads 64 contiguous bytes of
+// a weight row per 128-wide K block (16 rows x 256 B per wave), which the
+// matrix core consumes as four 16x16x32 bf16 products whose K chunks are
+// permuted the same way on both operands.  Activations are tiny and
+// L2-resident; an fp32 activation is split into a bf16 head and a bf16
+// remainder (two products), so the contraction keeps ~16 mantissa bits of it.
 #include "common.h"
 #include "kernels.h"
 
