@@ -333,3 +333,81 @@ def test_paged_decode_steps_with_the_page_pool():
     # the pool hands out exactly the pages the sequences' lengths need
     need = sum((int(tt) // r + 1 + page_rows - 1) // page_rows for tt in t - 1)
     assert alloc.available() == pool_pages - need
+
+
+def test_paged_pages_outside_the_pool_are_skipped():
+    """Table entries that are not pages of the pool (-1, or past its end)
+    are never read or written: an attended row on such a page is left out
+    (the same result as the contiguous layout with that selection removed),
+    an HCA query attends only the rows whose pages exist (the oracle over
+    those rows), an append into such a page writes nothing, and the indexer
+    still scores every row of the valid pages exactly."""
+    import compressed_sparse_attention_06_amd as csa
+    page_rows, Ncap, B = 256, 2048, 2
+    q, win, sink, rows = _attn_inputs(21, B, 1, Ncap, False)
+    pos = np.array([[2048 * 4 - 1], [1500 * 4 - 1]], np.int32)
+    vis = np.array([2048, 1500])
+    pool, table, tab = _paginate(rows, vis, page_rows, 22)
+    bad = tab.copy()
+    bad[0, 3] = -1                       # entries 768 .. 1023 of sequence 0
+    bad[1, 1] = pool.shape[0] // page_rows + 5   # entries 256 .. 511 of sequence 1: past the pool
+    bad_t = dev(bad)
+    dropped = [lambda e: 768 <= e < 1024, lambda e: 256 <= e < 512]
+    sel = np.stack([synth.random_selection(23, int(vis[b]), 512, b=b) for b in range(B)])[:, None]
+    sel_c = sel.copy()
+    for b in range(B):
+        sel_c[b, 0] = [e if e >= 0 and not dropped[b](e) else -1 for e in sel[b, 0]]
+    scale = 1 / math.sqrt(512)
+    want = torch.empty((B, 1, 64, 512), device="cuda")
+    got = torch.empty((B, 1, 64, 512), device="cuda")
+    csa.csa_sparse_attn(q, rows, dev(sel_c), win, dev(pos), sink, want, window=128, scale=scale, rope_dim=64)
+    csa.csa_sparse_attn_paged(q, pool, bad_t, dev(sel), win, dev(pos), sink, got, page_rows=page_rows, window=128,
+                              scale=scale, rope_dim=64)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
+
+    # HCA (ratio 16): the rows of the missing pages are left out
+    hpos = np.array([[2048 * 16 - 1], [1500 * 16 - 1]], np.int32)
+    out = torch.empty((B, 1, 64, 512), device="cuda")
+    csa.hca_attn_paged(q, pool, bad_t, win, dev(hpos), sink, out, page_rows=page_rows, ratio=16, window=128,
+                       scale=scale, rope_dim=64)
+    torch.cuda.synchronize()
+    g, qh, rh, wh, sk = host(out), host(q), host(rows), host(win), sink.cpu().numpy()
+    for b in range(B):
+        p = int(hpos[b, 0])
+        keep = np.array([e for e in range(int(vis[b])) if not dropped[b](e)])
+        wr = np.stack([wh[b, pp % 128] for pp in oracle.window_positions(p, 128)])
+        w_ = oracle.sparse_attn(qh[b, 0], rh[b], keep, wr, sk, scale, p, 64)
+        assert_attn(g[b, 0], w_, what=f"hca b={b}")
+
+    # an append whose page is missing writes nothing
+    D, r = 512, 4
+    rng = np.random.default_rng(24)
+    kv = dev_bf16(synth.bf16_bits(rng.standard_normal((B, 2 * r, D)).astype(np.float32)))
+    gate = dev_bf16(synth.bf16_bits(rng.standard_normal((B, 2 * r, D)).astype(np.float32)))
+    gamma = dev(np.ones(D, np.float32))
+    apos = dev(np.array([800 * r + r - 1, 300 * r + r - 1], np.int32))   # entries 800 (b=0), 300 (b=1)
+    before = pool.clone()
+    csa.csa_compress_paged(kv, gate, gamma, pool, bad_t, page_rows=page_rows, ratio=r, overlap=1, rope_dim=64,
+                           pos=apos)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(pool), _bits(before))
+
+    # the indexer: rows of valid pages scored exactly as in the contiguous layout
+    rngi = np.random.default_rng(25)
+    qi = dev_bf16(synth.bf16_bits(synth.unit_rms(rngi, (B, 1, 64, 128))))
+    w = dev((rngi.standard_normal((B, 1, 64)) / 128 ** 0.5 / 8).astype(np.float32))
+    icache = dev_bf16(synth.bf16_bits(synth.unit_rms(rngi, (B, Ncap, 128))))
+    ipool, itable, itab = _paginate(icache, vis, page_rows, 26)
+    ibad = itab.copy()
+    ibad[0, 3] = -1
+    ibad[1, 1] = ipool.shape[0] // page_rows + 5
+    sw = torch.empty((B, 1, Ncap), device="cuda")
+    sg = torch.empty((B, 1, Ncap), device="cuda")
+    csa.csa_index_score(qi, w, icache, dev(pos), sw, ratio=4)
+    csa.csa_index_score_paged(qi, w, ipool, dev(pos), sg, dev(ibad), page_rows=page_rows, ratio=4)
+    torch.cuda.synchronize()
+    for b in range(B):
+        ok = np.array([not dropped[b](e) for e in range(Ncap)])
+        assert torch.equal(sg[b, 0][torch.from_numpy(ok).cuda()], sw[b, 0][torch.from_numpy(ok).cuda()])
+        assert torch.isfinite(sg[b, 0][torch.from_numpy(~ok).cuda()][: int(vis[b])]).all()
