@@ -411,3 +411,51 @@ def test_paged_pages_outside_the_pool_are_skipped():
         ok = np.array([not dropped[b](e) for e in range(Ncap)])
         assert torch.equal(sg[b, 0][torch.from_numpy(ok).cuda()], sw[b, 0][torch.from_numpy(ok).cuda()])
         assert torch.isfinite(sg[b, 0][torch.from_numpy(~ok).cuda()][: int(vis[b])]).all()
+
+
+@pytest.mark.parametrize("kind,kv4,k", [("csa", True, 512), ("hca", False, 0), ("csa", False, 1024)])
+def test_paged_many_queries_against_the_oracle(kind, kv4, k):
+    """Prefill-sized calls on paged caches (one workgroup per query, the
+    persistent kernel being for contiguous bf16 caches): a quantised pool, HCA
+    over every visible row, and the Pro model's top-k 1024; sampled queries
+    against the oracle on the rows the pool holds (dequantised for the
+    quantised pool)."""
+    import compressed_sparse_attention_06_amd as csa
+    page_rows, Ncap, S = 128, 2048, 520
+    hca = kind == "hca"
+    r = 16 if hca else 4
+    pos = (np.arange(S) + (r * Ncap - 300 if hca else 4 * 1800)).astype(np.int32)[None]
+    Wcap = 4 * Ncap * (4 if hca else 1) + S + 8
+    vis = np.array([min((int(pos[0, -1]) + 1) // r, Ncap)])
+    q, win, sink, rows = _attn_inputs(31, 1, S, Ncap, False, Wcap=Wcap)
+    rows64 = host(rows)[0]
+    if kv4:
+        rb = csa.csa_kv4_row_bytes(512, 64)
+        q4 = torch.empty((1, Ncap, rb), dtype=torch.uint8, device="cuda")
+        csa.csa_kv4_quantize(rows, q4, rope_dim=64)
+        bytes_ = q4.cpu().numpy()[0]
+        from oracle import quant as Q
+        rows64 = np.stack([Q.dequantize_row(bytes_[e], 512, 64) for e in range(Ncap)])
+        rows = q4
+    pool, table, _ = _paginate(rows, vis, page_rows, 32)
+    out = torch.empty((1, S, 64, 512), device="cuda")
+    scale = 1 / math.sqrt(512)
+    if hca:
+        csa.hca_attn_paged(q, pool, table, win, dev(pos), sink, out, page_rows=page_rows, ratio=r, window=128,
+                           scale=scale, rope_dim=64)
+        sel = None
+    else:
+        sel = np.stack([synth.random_selection(33, min(oracle.visible(int(pos[0, s_]), r), Ncap), k, b=0, t=s_)
+                        for s_ in range(S)])[None]
+        csa.csa_sparse_attn_paged(q, pool, table, dev(sel), win, dev(pos), sink, out, page_rows=page_rows,
+                                  window=128, scale=scale, rope_dim=64)
+    torch.cuda.synchronize()
+    g, qh, wh, sk = host(out), host(q), host(win), sink.cpu().numpy()
+    for s_ in (0, 1, 257, S - 1):
+        p = int(pos[0, s_])
+        wr = np.stack([wh[0, pp % Wcap] for pp in oracle.window_positions(p, 128)])
+        if hca:
+            want = oracle.hca_attn(qh[0, s_], rows64, min(oracle.visible(p, r), Ncap), wr, sk, scale, p, 64)
+        else:
+            want = oracle.sparse_attn(qh[0, s_], rows64, sel[0, s_], wr, sk, scale, p, 64)
+        assert_attn(g[0, s_], want, what=f"{kind} query {s_}")
