@@ -906,8 +906,8 @@ def note(msg):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this path runs on a single MI355X (see the sharding notes in the design "
-              "document); --gpus above 1 is not supported", file=sys.stderr)
+        print("bench.py measures one GPU: this path runs on a single MI355X; --gpus above 1 is not supported",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
