@@ -459,3 +459,66 @@ def test_paged_many_queries_against_the_oracle(kind, kv4, k):
         else:
             want = oracle.sparse_attn(qh[0, s_], rows64, sel[0, s_], wr, sk, scale, p, 64)
         assert_attn(g[0, s_], want, what=f"{kind} query {s_}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_paged_vector_paths_match_contiguous(dtype):
+    """Shapes off the matrix cores (4 heads of 96, a 2 x 16 indexer, 96-wide
+    compressed rows) take the vector kernels, which translate rows through
+    the table one entry at a time: bit-identical to the contiguous layout."""
+    import compressed_sparse_attention_06_amd as csa
+    B, Ncap, page_rows, D, H, DI, HI = 2, 256, 64, 96, 4, 16, 2
+    rng = np.random.default_rng(41)
+
+    def t(x):
+        return dev_bf16(synth.bf16_bits(x)) if dtype == "bf16" else dev(x.astype(np.float32))
+
+    vis = np.array([256, 150])
+    pos = np.array([[4 * 256 - 1], [4 * 150 - 1]], np.int32)
+    # indexer
+    qi = t(synth.unit_rms(rng, (B, 1, HI, DI)))
+    w = dev((rng.standard_normal((B, 1, HI)) / 4).astype(np.float32))
+    icache = t(synth.unit_rms(rng, (B, Ncap, DI)))
+    ipool, itable, _ = _paginate(icache, vis, page_rows, 42)
+    sw = torch.empty((B, 1, Ncap), device="cuda")
+    sg = torch.empty((B, 1, Ncap), device="cuda")
+    csa.csa_index_score(qi, w, icache, dev(pos), sw, ratio=4)
+    csa.csa_index_score_paged(qi, w, ipool, dev(pos), sg, itable, page_rows=page_rows, ratio=4)
+    # attention, CSA and HCA
+    q = t(synth.unit_rms(rng, (B, 1, H, D)))
+    win = t(synth.unit_rms(rng, (B, 8, D)))
+    sink = dev(rng.standard_normal(H).astype(np.float32))
+    rows = t(synth.unit_rms(rng, (B, Ncap, D)))
+    pool, table, _ = _paginate(rows, vis, page_rows, 43)
+    sel = np.stack([synth.random_selection(44, int(vis[b]), 32, b=b) for b in range(B)])[:, None]
+    scale = 1 / math.sqrt(D)
+    outs = []
+    for paged in (False, True):
+        o1 = torch.empty((B, 1, H, D), device="cuda")
+        o2 = torch.empty((B, 1, H, D), device="cuda")
+        if paged:
+            csa.csa_sparse_attn_paged(q, pool, table, dev(sel), win, dev(pos), sink, o1, page_rows=page_rows, window=8,
+                                      scale=scale, rope_dim=32)
+            csa.hca_attn_paged(q, pool, table, win, dev(pos), sink, o2, page_rows=page_rows, ratio=4, window=8,
+                               scale=scale, rope_dim=32)
+        else:
+            csa.csa_sparse_attn(q, rows, dev(sel), win, dev(pos), sink, o1, window=8, scale=scale, rope_dim=32)
+            csa.hca_attn(q, rows, win, dev(pos), sink, o2, ratio=4, window=8, scale=scale, rope_dim=32)
+        outs.append((o1, o2))
+    # compressor (a 96-wide row is not a multiple of 128: the one-wave path)
+    kv = t(rng.standard_normal((B, 8, D)))
+    gate = t(rng.standard_normal((B, 8, D)))
+    gamma = dev((1 + 0.1 * rng.standard_normal(D)).astype(np.float32))
+    apos = dev(np.array([63 * 4 + 3, 64 * 4 + 3], np.int32))       # entries 63 and 64: two pages
+    cont = torch.zeros((B, Ncap, D), dtype=rows.dtype, device="cuda")
+    csa.csa_compress(kv, gate, gamma, cont, ratio=4, overlap=1, rope_dim=32, pos=apos)
+    cpool, ctable, ctab = _paginate(torch.zeros_like(cont), np.array([64, 65]), page_rows, 45)
+    csa.csa_compress_paged(kv, gate, gamma, cpool, ctable, page_rows=page_rows, ratio=4, overlap=1, rope_dim=32,
+                           pos=apos)
+    torch.cuda.synchronize()
+    assert torch.equal(sg, sw)
+    for a_, b_ in zip(outs[0], outs[1]):
+        assert torch.equal(a_, b_)
+    for b, e in ((0, 63), (1, 64)):
+        row = int(ctab[b, e // page_rows]) * page_rows + e % page_rows
+        assert torch.equal(_bits(cpool[row]), _bits(cont[b, e]))
