@@ -81,11 +81,15 @@ __global__ __launch_bounds__(kWave* kStreamWaves) void index_stream(IndexArgs a)
   // every load instruction covers 64 contiguous bytes of 16 rows
   auto load = [&](int step, uint4 (&kb)[4][4]) {
     const int64_t base = row0 + int64_t(step) * kStepRows + wave * 64;
+    // rows past the causal bound repeat the last visible row (finite, their
+    // scores are masked): every lane issues the same loads, so the counts of
+    // loads in flight are static and the operand's wait below stays short
+    const int64_t last = n_vis - 1;
     // a paged cache: the wave's 64 rows share one page (pages hold a
     // multiple of 64 rows); shift the base so that row e reads its pool row
     const uint16_t* cb = cache;
-    if (a.pt.pages && base < n_vis) {
-      const int64_t lp = base >> a.pt.page_shift;
+    if (a.pt.pages) {
+      const int64_t lp = (base < last ? base : last) >> a.pt.page_shift;
       const int pg = a.pt.pages[int64_t(b) * a.pt.max_pages + lp];
       // an unallocated or foreign page reads the pool's first page instead
       // (its scores are still written; such a table is the caller's error)
@@ -94,24 +98,29 @@ __global__ __launch_bounds__(kWave* kStreamWaves) void index_stream(IndexArgs a)
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
       const int64_t e = base + blk * 16 + r16;
-      if (e < n_vis) {
-        const uint4* src = reinterpret_cast<const uint4*>(cb + e * kDI) + g;
+      const uint4* src = reinterpret_cast<const uint4*>(cb + (e < last ? e : last) * kDI) + g;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kb[blk][ks] = src[ks * 4];
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kb[blk][ks] = uint4{0, 0, 0, 0};
-      }
+      for (int ks = 0; ks < 4; ++ks) kb[blk][ks] = src[ks * 4];
     }
   };
-  // the first step's rows are requested before the query operand is staged
+  // The query operand's loads go out first (16 KiB, mostly L2 hits), then the
+  // first step's rows: the wait before staging the operand in LDS covers only
+  // the operand, and the rows are scored block by block as they land.
+  // (Requested after the rows, the operand waited for every row -- loads
+  // complete in order -- so no product started before the last row arrived.)
+  // (two named registers per thread: an array here would be placed in LDS,
+  // whose store would then wait for the loads before the rows go out)
+  static_assert(kHI * kDI / 8 == 2 * kWave * kStreamWaves, "two operand slots per thread");
+  const uint4* qg = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q_idx) + qi * (kHI * kDI));
+  const int i0 = tid, i1 = tid + kWave * kStreamWaves;
+  const uint4 qv0 = qg[i0], qv1 = qg[i1];
+  const float wq = a.w[qi * kHI + tid % kHI];  // (every lane loads: no branch around the load)
+  __builtin_amdgcn_sched_barrier(0);  // (keeps the operand's loads ahead of the rows')
   uint4 kb0[4][4];
   load(0, kb0);
-  {
-    const uint4* q = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q_idx) + qi * (kHI * kDI));
-    for (int i = tid; i < kHI * kDI / 8; i += kWave * kStreamWaves) qs[(i / (kDI / 8)) * (kDI / 8 + 1) + i % (kDI / 8)] = q[i];
-    if (tid < kHI) wsh[tid] = a.w[qi * kHI + tid];
-  }
+  qs[(i0 / (kDI / 8)) * (kDI / 8 + 1) + i0 % (kDI / 8)] = qv0;
+  qs[(i1 / (kDI / 8)) * (kDI / 8 + 1) + i1 % (kDI / 8)] = qv1;
+  if (tid < kHI) wsh[tid] = wq;
   __syncthreads();
   bf16x8 qa[4][4];  // [head tile][K-step]: Q[mt*16 + r16][ks*32 + g*8 .. +7]
 #pragma unroll
