@@ -59,63 +59,97 @@ __global__ __launch_bounds__(kPThreads) void proj_gemm(ProjArgs a) {
   const int m0 = int(blockIdx.z) * rows;
   const bool live = n0 < a.N;  // a wave past the last row still helps stage
 
-  // 1. token rows of the chunk: loads first (weights queue behind them)
+  // 1. token rows of the chunk: loads first (weights queue behind them).
+  // Every thread issues the same loads (rows past the last token read the
+  // last token's row and are zeroed when staged): behind a per-thread branch
+  // the compiler waited for each load before issuing the next, a chain of
+  // round trips ahead of the weight stream.
   constexpr int per_thread = rows * kc / 4 / kPThreads;  // 4 values per slot
   static_assert(per_thread >= 1 && rows * kc / 4 % kPThreads == 0, "staging slots");
-  float xv[per_thread][4];
-#pragma unroll
-  for (int i = 0; i < per_thread; ++i) {
+  constexpr int RW = ACT_F32 ? 4 : 2;  // 32-bit words per slot
+  uint32_t xr[per_thread][RW];
+  auto slot_off = [&](int i, bool* valid) {
     const int slot = i * kPThreads + int(threadIdx.x);
     const int r = slot / (kc / 4), c = (slot % (kc / 4)) * 4;
     const int m = m0 + r;
-    const int64_t off = int64_t(grp) * a.a_goff + int64_t(m) * a.lda + k0 + c;
-    if (m < a.M) {
-      if constexpr (ACT_F32) {
-        const float* A = static_cast<const float*>(a.A);
-        float4 v = *reinterpret_cast<const float4*>(A + off);
-        for (int p = 1; p < a.a_nsum; ++p) {  // partial sums of the previous product, in order
-          const float4 u = *reinterpret_cast<const float4*>(A + off + p * a.a_kstride);
-          v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
-        }
-        xv[i][0] = v.x; xv[i][1] = v.y; xv[i][2] = v.z; xv[i][3] = v.w;
-      } else {
-        const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.A) + off);
-        xv[i][0] = bf16_lo(u.x); xv[i][1] = bf16_hi(u.x); xv[i][2] = bf16_lo(u.y); xv[i][3] = bf16_hi(u.y);
-      }
+    *valid = m < a.M;
+    return int64_t(grp) * a.a_goff + int64_t(m < a.M ? m : a.M - 1) * a.lda + k0 + c;
+  };
+#pragma unroll
+  for (int i = 0; i < per_thread; ++i) {
+    bool valid;
+    const int64_t off = slot_off(i, &valid);
+    if constexpr (ACT_F32) {
+      const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.A) + off);
+      xr[i][0] = v.x; xr[i][1] = v.y; xr[i][2] = v.z; xr[i][3] = v.w;
     } else {
-      xv[i][0] = xv[i][1] = xv[i][2] = xv[i][3] = 0.f;
+      const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.A) + off);
+      xr[i][0] = u.x; xr[i][1] = u.y;
     }
   }
+  __builtin_amdgcn_sched_barrier(0);  // (keeps the token rows' loads ahead of the weights')
   // 2. the wave's whole weight tile of the chunk: 64 contiguous bytes of one
-  // row per lane and K block
+  // row per lane and K block (issued by every wave: rows past the last read
+  // the last row, and their products are not stored)
   uint4 w[NKB][4];
-  if (live) {
+  {
+    const int nrow = n0 + c16 < a.N ? n0 + c16 : a.N - 1;
     const uint4* W = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.W) + int64_t(grp) * a.w_goff +
-                                                    int64_t(n0 + c16) * a.K + k0 + 32 * gq);
+                                                    int64_t(nrow) * a.K + k0 + 32 * gq);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int s = 0; s < 4; ++s) w[kb][s] = W[kb * (kKB / 8) + s];  // plain loads: measured faster than non-temporal
   }
-  // 3. stage the token rows (bf16, or a bf16 head and remainder)
+  // 3. fp32 rows that are partial sums of the previous product add their
+  // other parts, in order: one batch of loads per part, every slot at once
+  // (those loads queue behind the weights)
+  float v[per_thread][4];
+  if constexpr (ACT_F32) {
+#pragma unroll
+    for (int i = 0; i < per_thread; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[i][j] = __uint_as_float(xr[i][j]);
+    for (int p = 1; p < a.a_nsum; ++p) {
+      float4 u[per_thread];
+#pragma unroll
+      for (int i = 0; i < per_thread; ++i) {
+        bool valid;
+        const int64_t off = slot_off(i, &valid);
+        u[i] = *reinterpret_cast<const float4*>(static_cast<const float*>(a.A) + off + p * a.a_kstride);
+      }
+#pragma unroll
+      for (int i = 0; i < per_thread; ++i) {
+        v[i][0] += u[i].x; v[i][1] += u[i].y; v[i][2] += u[i].z; v[i][3] += u[i].w;
+      }
+    }
+  }
+  // 4. stage the token rows (bf16, or a bf16 head and remainder)
 #pragma unroll
   for (int i = 0; i < per_thread; ++i) {
+    bool valid;
+    (void)slot_off(i, &valid);
     const int slot = i * kPThreads + int(threadIdx.x);
     const int r = slot / (kc / 4), c = (slot % (kc / 4)) * 4;
-    uint32_t h0 = f32_to_bf16_bits(xv[i][0]), h1 = f32_to_bf16_bits(xv[i][1]);
-    uint32_t h2 = f32_to_bf16_bits(xv[i][2]), h3 = f32_to_bf16_bits(xv[i][3]);
-    *reinterpret_cast<uint2*>(&act[r * pitch + c]) = uint2{h0 | (h1 << 16), h2 | (h3 << 16)};
     if constexpr (ACT_F32) {
-      const uint32_t l0 = f32_to_bf16_bits(xv[i][0] - __uint_as_float(h0 << 16));
-      const uint32_t l1 = f32_to_bf16_bits(xv[i][1] - __uint_as_float(h1 << 16));
-      const uint32_t l2 = f32_to_bf16_bits(xv[i][2] - __uint_as_float(h2 << 16));
-      const uint32_t l3 = f32_to_bf16_bits(xv[i][3] - __uint_as_float(h3 << 16));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[i][j] = valid ? v[i][j] : 0.f;
+      const uint32_t h0 = f32_to_bf16_bits(v[i][0]), h1 = f32_to_bf16_bits(v[i][1]);
+      const uint32_t h2 = f32_to_bf16_bits(v[i][2]), h3 = f32_to_bf16_bits(v[i][3]);
+      *reinterpret_cast<uint2*>(&act[r * pitch + c]) = uint2{h0 | (h1 << 16), h2 | (h3 << 16)};
+      const uint32_t l0 = f32_to_bf16_bits(v[i][0] - __uint_as_float(h0 << 16));
+      const uint32_t l1 = f32_to_bf16_bits(v[i][1] - __uint_as_float(h1 << 16));
+      const uint32_t l2 = f32_to_bf16_bits(v[i][2] - __uint_as_float(h2 << 16));
+      const uint32_t l3 = f32_to_bf16_bits(v[i][3] - __uint_as_float(h3 << 16));
       *reinterpret_cast<uint2*>(&act[rows * pitch + r * pitch + c]) = uint2{l0 | (l1 << 16), l2 | (l3 << 16)};
+    } else {
+      // bf16 rows go to LDS as they are
+      *reinterpret_cast<uint2*>(&act[r * pitch + c]) = valid ? uint2{xr[i][0], xr[i][1]} : uint2{0u, 0u};
     }
   }
   __syncthreads();
   if (!live) return;
-  // 4. products: K chunk j of 8 (j = 4*gq + s within a K block) pairs the
+  // 5. products: K chunk j of 8 (j = 4*gq + s within a K block) pairs the
   // lane's weight bytes with the same 8 K values of token row c16
   floatx4 acc[MT];
 #pragma unroll
@@ -136,7 +170,7 @@ __global__ __launch_bounds__(kPThreads) void proj_gemm(ProjArgs a) {
       }
     }
   }
-  // 5. lane (c16, gq) holds rows n0 + 4*gq + i of token m0 + 16*t + c16
+  // 6. lane (c16, gq) holds rows n0 + 4*gq + i of token m0 + 16*t + c16
   const bool partial = a.ks_count > 1;
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
