@@ -229,9 +229,23 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int g = lane / 16, c16 = lane % 16;
+  const int64_t j_begin = int64_t(split) * chunk_rows;
+  // CSA: the chunk's selection entries are requested beside the position,
+  // as if the window were full (true for every query at or past its
+  // window'th token), so that one round trip brings both; a query with a
+  // shorter window reads its entries again below
+  constexpr int kSpecPer = (kMaxChunk + kThreads - 1) / kThreads;
+  int spec[kSpecPer];
+  if constexpr (!HCA) {
+#pragma unroll
+    for (int t = 0; t < kSpecPer; ++t) {
+      const int j = tid + t * kThreads;
+      const int64_t i = j_begin + j - a.window;
+      spec[t] = (j < chunk_rows && i >= 0 && i < a.k) ? a.idx[qi * a.k + i] : -1;
+    }
+  }
   const Cand c = candidates(a, HCA, qi);
   const int64_t n_cand = c.n_win + c.n_sel;
-  const int64_t j_begin = int64_t(split) * chunk_rows;
   const int n_rows = int(j_begin < n_cand ? (n_cand - j_begin < chunk_rows ? n_cand - j_begin : chunk_rows) : 0);
   const int n_tiles = (n_rows + kT - 1) / kT;
   const uint16_t* win = static_cast<const uint16_t*>(a.win) + int64_t(b) * a.Wcap * kD;
@@ -259,7 +273,19 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
   // on a dependent index load
   const bool resolved = !HCA || a.pt.pages != nullptr;  // HCA: contiguous rows need no table
   if (resolved) {
-    for (int j = tid; j < n_rows; j += kThreads) codes[j] = cand_code(a, HCA, c, qi, j_begin + j);
+#pragma unroll
+    for (int t = 0; t < kSpecPer; ++t) {
+      const int j = tid + t * kThreads;
+      if (j >= n_rows) continue;
+      int code;
+      if (!HCA && c.n_win == a.window && j_begin + j >= c.n_win) {
+        const int e = spec[t];  // the selection entry of candidate j_begin + j
+        code = (e >= 0 && e < a.Ncap) ? (a.pt.pages ? int(paged_row(a.pt, b, e)) : e) : -1;
+      } else {
+        code = cand_code(a, HCA, c, qi, j_begin + j);
+      }
+      codes[j] = code;
+    }
   }
   if (tid == 0) over_flag = 0;
   if (tid < kH) mref[tid] = sink_ref(a.sink, tid);
