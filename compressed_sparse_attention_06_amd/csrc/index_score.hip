@@ -67,6 +67,19 @@ __global__ __launch_bounds__(kWave* kStreamWaves) void index_stream(IndexArgs a)
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int g = lane / 16, r16 = lane % 16;
   const int Ncap = a.Ncap;
+  // The query operand (16 KiB, L2 hits when nothing else is in flight) is
+  // requested before anything else and staged in LDS before any row is
+  // requested.  Requested beside the rows, it waited behind the row traffic
+  // of the whole chip (an L2 hit then took 1-5 us instead of 0.2-0.6), and
+  // no product could start before it.
+  // (two named registers per thread: an array here would be placed in LDS,
+  // whose store would then wait for the loads)
+  static_assert(kHI * kDI / 8 == 2 * kWave * kStreamWaves, "two operand slots per thread");
+  const uint4* qg = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q_idx) + qi * (kHI * kDI));
+  const int i0 = tid, i1 = tid + kWave * kStreamWaves;
+  const uint4 qv0 = qg[i0], qv1 = qg[i1];
+  const float wq = a.w[qi * kHI + tid % kHI];  // (every lane loads: no branch around the load)
+  __builtin_amdgcn_sched_barrier(0);
   const int64_t n_vis = visible_entries(a.pos, qi, a.ratio, Ncap);
   const int64_t row0 = int64_t(blockIdx.y) * kStepRows * STEPS;
   float* srow = a.scores + qi * Ncap;
@@ -103,25 +116,13 @@ __global__ __launch_bounds__(kWave* kStreamWaves) void index_stream(IndexArgs a)
       for (int ks = 0; ks < 4; ++ks) kb[blk][ks] = src[ks * 4];
     }
   };
-  // The query operand's loads go out first (16 KiB, mostly L2 hits), then the
-  // first step's rows: the wait before staging the operand in LDS covers only
-  // the operand, and the rows are scored block by block as they land.
-  // (Requested after the rows, the operand waited for every row -- loads
-  // complete in order -- so no product started before the last row arrived.)
-  // (two named registers per thread: an array here would be placed in LDS,
-  // whose store would then wait for the loads before the rows go out)
-  static_assert(kHI * kDI / 8 == 2 * kWave * kStreamWaves, "two operand slots per thread");
-  const uint4* qg = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q_idx) + qi * (kHI * kDI));
-  const int i0 = tid, i1 = tid + kWave * kStreamWaves;
-  const uint4 qv0 = qg[i0], qv1 = qg[i1];
-  const float wq = a.w[qi * kHI + tid % kHI];  // (every lane loads: no branch around the load)
-  __builtin_amdgcn_sched_barrier(0);  // (keeps the operand's loads ahead of the rows')
-  uint4 kb0[4][4];
-  load(0, kb0);
   qs[(i0 / (kDI / 8)) * (kDI / 8 + 1) + i0 % (kDI / 8)] = qv0;
   qs[(i1 / (kDI / 8)) * (kDI / 8 + 1) + i1 % (kDI / 8)] = qv1;
   if (tid < kHI) wsh[tid] = wq;
   __syncthreads();
+  // then the first step's rows, scored block by block as they land
+  uint4 kb0[4][4];
+  load(0, kb0);
   bf16x8 qa[4][4];  // [head tile][K-step]: Q[mt*16 + r16][ks*32 + g*8 .. +7]
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
