@@ -443,9 +443,14 @@ __global__ __launch_bounds__(kDW * kWave) void index_dma(IndexArgs a) {
 // the sequence lengths (a grid of equal row ranges per query leaves CUs idle
 // at the end when lengths differ).  A wave streams its chunks through a
 // private four-slot LDS ring as index_dma does, loads the next query's
-// operands when its range enters that query, and sends its scores out in one
-// 1 KiB store per 256 rows.  Afterwards the workgroups share the -inf fill of
-// every row past a query's last chunk.
+// operands when its range enters that query, and gathers its scores 256 rows
+// at a time.  A full buffer of scores is parked in registers (up to 16 per
+// wave) and written once the wave's stream is done: score stores issued in
+// the middle of the stream cost far more than their bytes (each one holds
+// the wave's in-order load count until it is acknowledged, and the writes
+// interleave with the row reads), about 9 % of the kernel at a 1M-token
+// context.  Afterwards the workgroups share the -inf fill of every row past
+// a query's last chunk.
 // PAGED: the rows live in a page pool (pages of a power-of-two multiple of 64
 // rows, so a 16-row chunk never straddles two); the issuing cursor keeps the
 // pool page of its current logical page and, on entering a page, requests
@@ -453,6 +458,7 @@ __global__ __launch_bounds__(kDW * kWave) void index_dma(IndexArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kFlatMaxQ = 1024;  // queries whose chunk counts fit in LDS
 constexpr int kFlush = 256;      // score rows per store
+constexpr int kSeg = 16;         // score segments a wave keeps until its stream ends
 
 // s_waitcnt vmcnt(n) for a run-time n in 0..15
 __device__ __forceinline__ void wait_vmem_upto15(int n) {
@@ -483,6 +489,7 @@ __global__ __launch_bounds__(kDW * kWave) void index_flat(IndexArgs a) {
   __shared__ int64_t cpre[kFlatMaxQ + 1];  // chunks of the queries before q
   __shared__ int64_t dpre[kFlatMaxQ + 1];  // 4-row groups past the chunks of the queries before q
   __shared__ int nvis_s[kFlatMaxQ];
+  __shared__ int seg_meta[kDW][kSeg][3];  // query, first row, rows of each parked segment
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int g = lane / 16, r16 = lane % 16;
@@ -624,10 +631,27 @@ __global__ __launch_bounds__(kDW * kWave) void index_flat(IndexArgs a) {
     for (int ks = 0; ks < 4; ++ks) koff[ks] = r16 * kRowB + (((ks * 4 + g) ^ r16) << 4);
     int sq = cc.q, sb = cc.lc * kDChunk, cnt = 0;  // buffered scores: rows sb .. sb+cnt-1 of query sq
     int f1 = 0, f2 = 0;                            // stores issued in the previous two iterations
-    auto flush = [&]() {
+    float4 seg[kSeg];
+    int nseg = 0;
+    // park the buffered scores in a register segment (no memory traffic), or
+    // store them when every segment is taken; true if a store was issued
+    auto flush = [&]() -> bool {
+      const float4 v = *reinterpret_cast<const float4*>(&sc[wave][4 * lane]);
+      if (nseg < kSeg) {
+#pragma unroll
+        for (int t = 0; t < kSeg; ++t)
+          if (t == nseg) seg[t] = v;
+        if (lane == 0) {
+          seg_meta[wave][nseg][0] = sq;
+          seg_meta[wave][nseg][1] = sb;
+          seg_meta[wave][nseg][2] = cnt;
+        }
+        ++nseg;
+        return false;
+      }
       if (4 * lane < cnt && sb + 4 * lane < Ncap)
-        *reinterpret_cast<float4*>(a.scores + int64_t(sq) * Ncap + sb + 4 * lane) =
-            *reinterpret_cast<const float4*>(&sc[wave][4 * lane]);
+        *reinterpret_cast<float4*>(a.scores + int64_t(sq) * Ncap + sb + 4 * lane) = v;
+      return true;
     };
     for (int j = 0; j < n; ++j) {
       // chunk j's copies are done; what was issued after them may still fly:
@@ -667,8 +691,7 @@ __global__ __launch_bounds__(kDW * kWave) void index_flat(IndexArgs a) {
       // scores leave when the buffer is full or the chunk starts another query
       int f0 = 0;
       if (cnt > 0 && (cc.q != sq || cnt == kFlush)) {
-        flush();
-        f0 = 1;
+        f0 = flush() ? 1 : 0;
         sq = cc.q;
         sb = cc.lc * kDChunk;
         cnt = 0;
@@ -686,6 +709,15 @@ __global__ __launch_bounds__(kDW * kWave) void index_flat(IndexArgs a) {
       }
     }
     flush();
+    // the parked segments leave together once the stream is done
+#pragma unroll
+    for (int t = 0; t < kSeg; ++t) {
+      if (t < nseg) {
+        const int q = seg_meta[wave][t][0], e0 = seg_meta[wave][t][1], m = seg_meta[wave][t][2];
+        if (4 * lane < m && e0 + 4 * lane < Ncap)
+          *reinterpret_cast<float4*>(a.scores + int64_t(q) * Ncap + e0 + 4 * lane) = seg[t];
+      }
+    }
   }
 
   // -inf past every query's last chunk, in float4 groups shared by all workgroups
