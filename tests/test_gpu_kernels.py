@@ -519,6 +519,56 @@ def test_hca_attn_mfma():
     assert_attn(host(out), want, what="hca")
 
 
+@pytest.mark.parametrize("case", ["csa8", "hca4", "csa100"])
+def test_split_decode_shapes(case):
+    """The split decode path at the bench's split counts (CSA: 8 queries in
+    10 splits; HCA: 4 queries in 52) and at 100 queries in 3 splits: each
+    matches the oracle, and three calls on one workspace give the same
+    bits."""
+    csa = csa_mod()
+    D, window, Wcap = 512, 128, 128
+    hca = case == "hca4"
+    if hca:
+        B, Ncap, k, r = 4, 8192, 4, 128
+        pos = np.array([[Ncap * r - 1], [6000 * r + 5], [100 * r - 1], [77]], np.int32)
+        only = None
+    elif case == "csa8":
+        B, Ncap, k, r = 8, 16384, 512, 4
+        pos = np.array([[4 * Ncap - 1], [4 * 9000 + 3], [130], [5000], [4 * Ncap - 2], [600], [127], [4 * 12345]],
+                       np.int32)
+        only = None
+    else:
+        B, Ncap, k, r = 100, 2048, 512, 4
+        pos = np.random.default_rng(5).integers(600, 4 * Ncap, (B, 1)).astype(np.int32)
+        only = {(b, 0) for b in (0, 1, 37, 64, 98, 99)}
+    q, cmp, win, sink, sel = _attn_case(B, 1, Ncap, k, window, Wcap, pos, 71)
+    scale = 1 / math.sqrt(D)
+    want = _oracle_attn(q, cmp, win, sink, None if hca else sel, pos, window, Wcap, scale, 64,
+                        hca_ratio=r if hca else None, only=only)
+    size = (csa.hca_attn_workspace_size(B, 1, 64, D, Ncap, window) if hca else
+            csa.csa_sparse_attn_workspace_size(B, 1, 64, D, k, window))
+    ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+    args = (dev_bf16(q), dev_bf16(cmp), dev_bf16(win), dev(pos), dev(sink)) if hca else \
+        (dev_bf16(q), dev_bf16(cmp), dev(sel), dev_bf16(win), dev(pos), dev(sink))
+    outs = []
+    for _ in range(3):
+        out = torch.empty((B, 1, 64, D), device="cuda")
+        if hca:
+            csa.hca_attn(*args, out, ratio=r, window=window, scale=scale, rope_dim=64, ws=ws)
+        else:
+            csa.csa_sparse_attn(*args, out, window=window, scale=scale, rope_dim=64, ws=ws)
+        torch.cuda.synchronize()
+        outs.append(out.cpu())
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0]), "repeated calls differ"
+    got = host(outs[0])
+    if only is not None:
+        idx = sorted(only)
+        got = np.stack([got[b, s] for b, s in idx])
+        want = np.stack([want[b, s] for b, s in idx])
+    assert_attn(got, want, what=case)
+
+
 def _scaled_bf16(bits, factor):
     return synth.bf16_bits((synth.bf16_to_f32(bits) * factor).astype(np.float32))
 
