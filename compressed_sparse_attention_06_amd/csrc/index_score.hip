@@ -7,16 +7,22 @@
 //
 // Every 256-byte index row meets 64 heads x 128 dims: 64 flop per byte, more
 // than a vector-ALU roofline can stream at HBM rate, so the 64 heads form the
-// M side of a bf16 matrix-core product even for a single query.  Two kernels:
+// M side of a bf16 matrix-core product even for a single query.  Kernels:
 //
-//  * index_stream (few queries, e.g. decode): each wave keeps the query's
-//    64x128 operand in registers and streams 64 index rows per step straight
-//    from HBM into registers (every load instruction covers 64 contiguous
-//    bytes of 16 rows), 4 x 16x16x32 MFMA per 16 rows and K-step, then ReLU,
-//    head weights and a two-step cross-lane sum.
+//  * index_stream (few queries over short caches, e.g. a 64K-token decode):
+//    each wave keeps the query's 64x128 operand in registers and loads its
+//    64 index rows straight from HBM into registers (every load instruction
+//    covers 64 contiguous bytes of 16 rows), 4 x 16x16x32 MFMA per 16 rows
+//    and K-step, then ReLU, head weights and a two-step cross-lane sum.
+//  * index_flat (up to 1,024 queries over >= 2M rows in all, e.g. a 1M-token
+//    decode batch): one persistent workgroup per CU; every wave streams an
+//    equal share of all queries' visible rows through a private LDS ring.
+//  * index_dma (more queries over long caches): the same ring per wave over
+//    a fixed row range of one query.
 //  * index_tile (many queries per sequence, e.g. prefill): the query
 //    operands stay in registers and the index rows stream past them through
 //    LDS up to the workgroup's causal bound.
+//  * index_any: other shapes and fp32, on the vector ALU.
 //
 // A and B share the K order of a K-step: lane group g, element i <-> dim
 // ks*32 + g*8 + i.
