@@ -67,7 +67,6 @@ int page_table(const csa_page_table* t, csa::PageTable* out) {
 // Validates one compressor call and fills its kernel arguments and plan.
 int compress_job(const csa_compress_job& j, csa::CompressArgs* out_args, csa::CompressPlan* out_plan,
                  const csa::PageTable* pt = nullptr) {
-  if (!j.kv || !j.gate || !j.gamma || !j.out) return CSA_ERR_INVALID_ARG;
   if (!dtype_ok(j.in_dtype) || !(dtype_ok(j.out_dtype) || j.out_dtype == CSA_KV4)) return CSA_ERR_INVALID_ARG;
   if (j.out_dtype == CSA_KV4 && !kv4_shape_ok(j.D, j.rope_dim)) return CSA_ERR_INVALID_ARG;
   if (j.B < 0 || j.T < 1 || j.D < 1 || j.ratio < 1 || (j.overlap != 0 && j.overlap != 1)) return CSA_ERR_INVALID_ARG;
@@ -83,9 +82,11 @@ int compress_job(const csa_compress_job& j, csa::CompressArgs* out_args, csa::Co
     return CSA_ERR_INVALID_ARG;
   if (j.D > 8192) return CSA_ERR_UNSUPPORTED;
   if (j.pos == nullptr) {
-    if (j.tok0 < 0 || j.e0 < 0 || j.n_entries < 0 || int64_t(j.e0) + j.n_entries > j.out_cap)
-      return CSA_ERR_INVALID_ARG;
-    if (j.n_entries > 0) {
+    if (j.tok0 < 0 || j.e0 < 0 || j.n_entries < 0) return CSA_ERR_INVALID_ARG;
+    // (with no sequence nothing is built: an empty ring-mode batch, whose pos
+    // is NULL, lands here and its entry range bounds nothing)
+    if (j.B > 0 && int64_t(j.e0) + j.n_entries > j.out_cap) return CSA_ERR_INVALID_ARG;
+    if (j.B > 0 && j.n_entries > 0) {
       const int64_t lo = (int64_t(j.e0) - ((j.overlap && j.e0 > 0) ? 1 : 0)) * j.ratio;
       const int64_t hi = (int64_t(j.e0) + j.n_entries) * j.ratio;
       if (lo < j.tok0 || hi > int64_t(j.tok0) + j.T) return CSA_ERR_INVALID_ARG;
@@ -95,6 +96,9 @@ int compress_job(const csa_compress_job& j, csa::CompressArgs* out_args, csa::Co
   }
   const int64_t entries = j.pos == nullptr ? int64_t(j.B) * j.n_entries : j.B;
   if (entries > INT32_MAX) return CSA_ERR_UNSUPPORTED;
+  // a call that builds no entry reads and writes nothing: its pointers may be NULL
+  const bool none = entries == 0;
+  if (!none && (!j.kv || !j.gate || !j.gamma || !j.out)) return CSA_ERR_INVALID_ARG;
   const csa::CompressPlan plan = csa::plan_compress(entries, j.D, j.ratio, j.overlap);
   // the lane kernel reads and writes rows with 16-byte accesses: a misaligned
   // tensor there is rejected rather than sent down a much slower path
@@ -105,7 +109,7 @@ int compress_job(const csa_compress_job& j, csa::CompressArgs* out_args, csa::Co
         (j.in_bstride * esize(j.in_dtype)) % 16 != 0 || (j.out_bstride * esize(j.out_dtype)) % 16 != 0)
       return CSA_ERR_INVALID_ARG;
   }
-  if (plan.ws_bytes > 0 && (j.ws == nullptr || j.ws_bytes < plan.ws_bytes)) return CSA_ERR_WORKSPACE;
+  if (!none && plan.ws_bytes > 0 && (j.ws == nullptr || j.ws_bytes < plan.ws_bytes)) return CSA_ERR_WORKSPACE;
   if (plan.ws_bytes > 0 && !aligned16(j.ws)) return CSA_ERR_INVALID_ARG;
   csa::CompressArgs a{};
   a.kv = j.kv;
@@ -167,12 +171,16 @@ int csa_compress_paged(const csa_compress_job* jobs, const csa_page_table* table
   csa::CompressArgs a[CSA_MAX_COMPRESS_JOBS];
   csa::CompressPlan plan[CSA_MAX_COMPRESS_JOBS];
   for (int i = 0; i < n_jobs; ++i) {
-    csa::PageTable pt;
-    int st = page_table(&tables[i], &pt);
-    if (st != CSA_OK) return st;
+    csa::PageTable pt{};
     csa_compress_job j = jobs[i];
-    j.out_cap = tables[i].max_pages * tables[i].page_rows;  // the logical capacity of a sequence
-    st = compress_job(j, &a[i], &plan[i], &pt);
+    if (j.B == 0 || (j.pos == nullptr && j.n_entries == 0)) {
+      j.out_cap = INT32_MAX;  // a job that builds no entry reads no page table and bounds nothing
+    } else {
+      const int st = page_table(&tables[i], &pt);
+      if (st != CSA_OK) return st;
+      j.out_cap = tables[i].max_pages * tables[i].page_rows;  // the logical capacity of a sequence
+    }
+    const int st = compress_job(j, &a[i], &plan[i], &pt);
     if (st != CSA_OK) return st;
   }
   return hip_status(csa::launch_compress(a, plan, n_jobs, stream));
@@ -195,9 +203,11 @@ namespace {
 
 int index_common(const void* q_idx, const float* w, const void* idx_cache, int dtype, const int* pos, int B, int S,
                  int H_I, int D_I, int Ncap, int ratio, float* scores, const csa::PageTable* pt, hipStream_t stream) {
-  if (!q_idx || !w || !idx_cache || !pos || !scores) return CSA_ERR_INVALID_ARG;
   if (!dtype_ok(dtype) || B < 0 || S < 0 || H_I < 1 || D_I < 1 || Ncap < 0 || ratio < 1) return CSA_ERR_INVALID_ARG;
   if (int64_t(B) * S > INT32_MAX || (int64_t(Ncap) + 255) / 256 > kMaxGridY) return CSA_ERR_UNSUPPORTED;
+  // no query or no cache row: nothing is read or written, the pointers may be NULL
+  const bool none = int64_t(B) * S == 0 || Ncap == 0;
+  if (!none && (!q_idx || !w || !idx_cache || !pos || !scores)) return CSA_ERR_INVALID_ARG;
   // matrix-core shape: 16-byte operand loads and score stores in 16-byte
   // groups, so misaligned tensors are rejected (not run on the vector path)
   const bool mfma = dtype == CSA_BF16 && H_I == 64 && D_I == 128;
@@ -233,7 +243,9 @@ int csa_index_score(const void* q_idx, const float* w, const void* idx_cache, in
 int csa_index_score_paged(const void* q_idx, const float* w, const void* idx_pool, int dtype, const int* pos, int B,
                           int S, int H_I, int D_I, const csa_page_table* pages, int ratio, float* scores,
                           hipStream_t stream) {
-  csa::PageTable pt;
+  csa::PageTable pt{};
+  if (int64_t(B) * S == 0)  // no query: the page table is not read
+    return index_common(q_idx, w, idx_pool, dtype, pos, B, S, H_I, D_I, 0, ratio, scores, &pt, stream);
   const int st = page_table(pages, &pt);
   if (st != CSA_OK) return st;
   return index_common(q_idx, w, idx_pool, dtype, pos, B, S, H_I, D_I, pages->max_pages * pages->page_rows, ratio,
@@ -247,7 +259,9 @@ size_t csa_topk_workspace_size(int R, int N, int k) {
 
 int csa_topk(const float* scores, const int* n_valid, int R, int N, int k, int* idx, void* ws, size_t ws_bytes,
              hipStream_t stream) {
-  if (!scores || !idx || R < 0 || N < 0 || k < 1 || k > 4096) return CSA_ERR_INVALID_ARG;
+  if (R < 0 || N < 0 || k < 1 || k > 4096) return CSA_ERR_INVALID_ARG;
+  // no row: nothing is read or written; rows of no position read no score
+  if (R > 0 && (!idx || (N > 0 && !scores))) return CSA_ERR_INVALID_ARG;
   if (R > INT32_MAX / 2) return CSA_ERR_UNSUPPORTED;
   const csa::TopkPlan plan = csa::plan_topk(R, N, k);
   if (plan.ws_bytes > 0 && (ws == nullptr || ws_bytes < plan.ws_bytes)) return CSA_ERR_WORKSPACE;
@@ -256,7 +270,9 @@ int csa_topk(const float* scores, const int* n_valid, int R, int N, int k, int* 
 }
 
 int csa_topk_noalloc(const float* scores, const int* n_valid, int R, int N, int k, int* idx, hipStream_t stream) {
-  if (!scores || !idx || R < 0 || N < 0 || k < 1 || k > 4096) return CSA_ERR_INVALID_ARG;
+  if (R < 0 || N < 0 || k < 1 || k > 4096) return CSA_ERR_INVALID_ARG;
+  // no row: nothing is read or written; rows of no position read no score
+  if (R > 0 && (!idx || (N > 0 && !scores))) return CSA_ERR_INVALID_ARG;
   if (R > INT32_MAX / 2) return CSA_ERR_UNSUPPORTED;
   if ((int64_t(N) + 16383) / 16384 > kMaxGridY) return CSA_ERR_UNSUPPORTED;
   const csa::TopkPlan plan = csa::plan_topk(R, N, k);
@@ -272,7 +288,6 @@ int attn_common(const void* q, const void* cmp, int Ncap, const int* idx, int k,
                 int window, const int* pos, const float* sink, int dtype, float scale, int rope_dim, float rope_base,
                 int B, int S, int H, int D, void* out, int out_dtype, void* ws, size_t ws_bytes, bool hca,
                 hipStream_t stream, const csa::PageTable* pt = nullptr) {
-  if (!q || !cmp || !pos || !sink || !out || (!hca && !idx) || (window > 0 && !win)) return CSA_ERR_INVALID_ARG;
   if (!(dtype_ok(dtype) || dtype == CSA_KV4) || !dtype_ok(out_dtype)) return CSA_ERR_INVALID_ARG;
   if (dtype == CSA_KV4 && (!kv4_shape_ok(D, rope_dim) || !aligned16(cmp))) return CSA_ERR_INVALID_ARG;
   if (B < 0 || S < 0 || H < 1 || D < 2 || Ncap < 0 || window < 0 || Wcap < window || (!hca && k < 0) ||
@@ -282,6 +297,9 @@ int attn_common(const void* q, const void* cmp, int Ncap, const int* idx, int k,
   if (rope_dim < 0 || rope_dim % 2 != 0 || rope_dim > D) return CSA_ERR_INVALID_ARG;
   if (!std::isfinite(scale) || !(rope_base > 0.f) || !std::isfinite(rope_base)) return CSA_ERR_INVALID_ARG;
   if (int64_t(B) * S > INT32_MAX) return CSA_ERR_UNSUPPORTED;
+  // no query: nothing is read or written, the pointers may be NULL
+  if (int64_t(B) * S == 0) return CSA_OK;
+  if (!q || !cmp || !pos || !sink || !out || (!hca && !idx) || (window > 0 && !win)) return CSA_ERR_INVALID_ARG;
   const int64_t max_cand = int64_t(window) + (hca ? Ncap : k);
   if (max_cand > INT32_MAX) return CSA_ERR_UNSUPPORTED;
   csa::AttnPlan plan = csa::plan_attn(B, S, H, D, window, hca ? Ncap : k, dtype, hca, pt != nullptr);
@@ -369,10 +387,11 @@ int csa_sparse_attn_paged(const void* q, const void* cmp_pool, const csa_page_ta
                           const void* win, int Wcap, int window, const int* pos, const float* sink, int dtype,
                           float scale, int rope_dim, float rope_base, int B, int S, int H, int D, void* out,
                           int out_dtype, void* ws, size_t ws_bytes, hipStream_t stream) {
-  csa::PageTable pt;
-  const int st = page_table(pages, &pt);
+  csa::PageTable pt{};
+  const bool none = int64_t(B) * S == 0;  // no query: the page table is not read
+  const int st = none ? CSA_OK : page_table(pages, &pt);
   if (st != CSA_OK) return st;
-  return attn_common(q, cmp_pool, pages->max_pages * pages->page_rows, idx, k, 1, win, Wcap, window, pos, sink, dtype,
+  return attn_common(q, cmp_pool, none ? 0 : pages->max_pages * pages->page_rows, idx, k, 1, win, Wcap, window, pos, sink, dtype,
                      scale, rope_dim, rope_base, B, S, H, D, out, out_dtype, ws, ws_bytes, false, stream, &pt);
 }
 
@@ -380,10 +399,11 @@ int hca_attn_paged(const void* q, const void* cmp_pool, const csa_page_table* pa
                    int Wcap, int window, const int* pos, const float* sink, int dtype, float scale, int rope_dim,
                    float rope_base, int B, int S, int H, int D, void* out, int out_dtype, void* ws, size_t ws_bytes,
                    hipStream_t stream) {
-  csa::PageTable pt;
-  const int st = page_table(pages, &pt);
+  csa::PageTable pt{};
+  const bool none = int64_t(B) * S == 0;  // no query: the page table is not read
+  const int st = none ? CSA_OK : page_table(pages, &pt);
   if (st != CSA_OK) return st;
-  return attn_common(q, cmp_pool, pages->max_pages * pages->page_rows, nullptr, 0, ratio, win, Wcap, window, pos, sink,
+  return attn_common(q, cmp_pool, none ? 0 : pages->max_pages * pages->page_rows, nullptr, 0, ratio, win, Wcap, window, pos, sink,
                      dtype, scale, rope_dim, rope_base, B, S, H, D, out, out_dtype, ws, ws_bytes, true, stream, &pt);
 }
 
@@ -529,8 +549,9 @@ size_t csa_kv4_row_bytes(int D, int rope_dim) {
 }
 
 int csa_kv4_quantize(const void* x, int x_dtype, int64_t rows, int D, int rope_dim, void* out, hipStream_t stream) {
-  if (!x || !out || !dtype_ok(x_dtype) || rows < 0 || D < 1 || rope_dim < 0 || !kv4_shape_ok(D, rope_dim))
+  if (!dtype_ok(x_dtype) || rows < 0 || D < 1 || rope_dim < 0 || !kv4_shape_ok(D, rope_dim))
     return CSA_ERR_INVALID_ARG;
+  if (rows > 0 && (!x || !out)) return CSA_ERR_INVALID_ARG;  // no row: the pointers may be NULL
   if (D > 8192 || (rows + 3) / 4 > INT32_MAX) return CSA_ERR_UNSUPPORTED;
   if (!aligned16(out)) return CSA_ERR_INVALID_ARG;
   const csa::Kv4Args a{x, x_dtype, rows, D, rope_dim, csa::kv4_row_bytes(D, rope_dim), out};
@@ -547,7 +568,6 @@ size_t csa_q_proj_workspace_size(int M, int d_model, int q_rank, int H, int head
 int csa_q_proj(const void* x, const void* wq_a, const float* gamma_q, const void* wq_b, const int* pos, int M,
                int d_model, int q_rank, int H, int head_dim, int rope_dim, float rope_base, float eps, void* q,
                void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!x || !wq_a || !gamma_q || !wq_b || !q || (M > 0 && rope_dim > 0 && !pos)) return CSA_ERR_INVALID_ARG;
   if (M < 0 || d_model < 1 || q_rank < 1 || H < 1 || head_dim < 2) return CSA_ERR_INVALID_ARG;
   if (rope_dim < 0 || rope_dim % 2 != 0 || rope_dim > head_dim) return CSA_ERR_INVALID_ARG;
   if (!(eps >= 0.f) || !std::isfinite(eps) || !(rope_base > 0.f) || !std::isfinite(rope_base))
@@ -558,11 +578,12 @@ int csa_q_proj(const void* x, const void* wq_a, const float* gamma_q, const void
       head_dim > 16384)
     return CSA_ERR_UNSUPPORTED;
   if (int64_t(M) > 65535 * 32) return CSA_ERR_UNSUPPORTED;
+  if (M == 0) return CSA_OK;  // no token: nothing is read or written, the pointers may be NULL
+  if (!x || !wq_a || !gamma_q || !wq_b || !q || (rope_dim > 0 && !pos)) return CSA_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(wq_a) || !aligned16(wq_b) || !aligned16(q)) return CSA_ERR_INVALID_ARG;
   const size_t need = csa_q_proj_workspace_size(M, d_model, q_rank, H, head_dim);
   if (need > 0 && (ws == nullptr || ws_bytes < need)) return CSA_ERR_WORKSPACE;
   if (need > 0 && !aligned16(ws)) return CSA_ERR_INVALID_ARG;
-  if (M == 0) return CSA_OK;
   const QPlan pl = q_plan(M, d_model, q_rank, hq);
   float* part1 = static_cast<float*>(ws);
   float* qrn = part1 + pl.part1;
@@ -598,7 +619,6 @@ size_t csa_out_proj_workspace_size(int M, int H, int head_dim, int groups, int o
 int csa_out_proj(const void* o, int o_dtype, const void* wo_a, const void* wo_b, int M, int H, int head_dim,
                  int groups, int o_rank, int d_model, void* y, int y_dtype, void* ws, size_t ws_bytes,
                  hipStream_t stream) {
-  if (!o || !wo_a || !wo_b || !y) return CSA_ERR_INVALID_ARG;
   if (!dtype_ok(o_dtype) || !dtype_ok(y_dtype)) return CSA_ERR_INVALID_ARG;
   if (M < 0 || H < 1 || head_dim < 1 || groups < 1 || o_rank < 1 || d_model < 1) return CSA_ERR_INVALID_ARG;
   const int64_t hd = int64_t(H) * head_dim;
@@ -607,11 +627,12 @@ int csa_out_proj(const void* o, int o_dtype, const void* wo_a, const void* wo_b,
   if (kg > INT32_MAX || kb > INT32_MAX) return CSA_ERR_UNSUPPORTED;
   if (!proj_dims_ok(M, o_rank, int(kg)) || !proj_dims_ok(M, d_model, int(kb))) return CSA_ERR_UNSUPPORTED;
   if (int64_t((o_rank + 127) / 128) * groups > 0x7fffffff || int64_t(M) > 65535 * 32) return CSA_ERR_UNSUPPORTED;
+  if (M == 0) return CSA_OK;  // no token: nothing is read or written, the pointers may be NULL
+  if (!o || !wo_a || !wo_b || !y) return CSA_ERR_INVALID_ARG;
   if (!aligned16(o) || !aligned16(wo_a) || !aligned16(wo_b) || !aligned16(y)) return CSA_ERR_INVALID_ARG;
   const size_t need = csa_out_proj_workspace_size(M, H, head_dim, groups, o_rank, d_model, o_dtype);
   if (need > 0 && (ws == nullptr || ws_bytes < need)) return CSA_ERR_WORKSPACE;
   if (need > 0 && !aligned16(ws)) return CSA_ERR_INVALID_ARG;
-  if (M == 0) return CSA_OK;
   const OPlan pl = o_plan(M, groups, o_rank, kg, d_model, o_dtype == CSA_F32);
   float* r = static_cast<float*>(ws);
   float* yp = r + pl.r;

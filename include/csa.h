@@ -31,6 +31,14 @@
  *     pos * rope_base^(-2i/rope_dim); the angle is formed and reduced in
  *     double precision.  A compressed entry e of ratio r sits at position
  *     e*r.
+ *   - A call with no work returns CSA_OK after checking its scalar arguments,
+ *     reads and writes nothing and makes no HIP call; its pointers may then
+ *     be NULL (as for empty tensors), the page table included.  No work
+ *     means: csa_compress* builds no entry (B = 0, or n_entries = 0 without
+ *     pos); csa_index_score* has B*S = 0 or no cache row; csa_topk* has
+ *     R = 0; the attention calls have B*S = 0; csa_kv4_quantize has
+ *     rows = 0; the projections have M = 0.  csa_topk* also accepts NULL
+ *     scores when N = 0 (every selection is then -1).
  *   - Return value: CSA_OK, or a negative CSA_ERR_* code.  Arguments are
  *     validated on the host before any HIP call, so a rejected call has no
  *     side effect.  Index values read from device memory (positions,

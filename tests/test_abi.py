@@ -272,3 +272,54 @@ def test_out_proj_validation(lib):
     assert _oproj(lib, G=8, R=8) == UNSUPPORTED          # o_rank 8: not a multiple of 16
     assert _oproj(lib, G=8, R=24) == UNSUPPORTED         # 8 x 24 = 192: K of the second product off 128
     assert _oproj(lib, ws_bytes=100) == WORKSPACE
+
+
+def test_calls_with_no_work_accept_null_pointers(lib):
+    """A call with no work checks its scalar arguments, then returns ok without
+    any HIP call (so it runs here); its pointers may be NULL, as torch passes
+    for empty tensors.  Bad scalars are still rejected."""
+    from compressed_sparse_attention_06_amd._lib import CompressJob, PageTableC
+    none = dict(kv=None, gate=None, gamma=None, out=None)
+    assert _compress(lib, B=0, **none) == 0
+    assert _compress(lib, n_entries=0, **none) == 0                       # span mode, no entry to build
+    hca = dict(ratio=128, overlap=0, T=128, in_bstride=128 * 512)       # a split plan: no workspace needed either
+    assert _compress(lib, B=0, pos=P, **hca, **none) == 0
+    assert _compress(lib, B=0, n_entries=4, **hca, **none) == 0          # an empty ring batch: torch's pos is NULL
+    assert _compress(lib, B=0, ratio=0, **none) == INVALID
+    assert _compress(lib, B=0, D=0, **none) == INVALID
+    nul = dict(q=None, w=None, cache=None, pos=None, scores=None)
+    assert _index(lib, B=0, **nul) == 0
+    assert _index(lib, S=0, **nul) == 0
+    assert _index(lib, Ncap=0, **nul) == 0
+    assert _index(lib, B=0, ratio=0, **nul) == INVALID
+    assert lib.csa_topk(None, None, 0, 10, 4, None, None, 0, None) == 0
+    assert lib.csa_topk(None, None, 0, 262144, 512, None, None, 0, None) == 0   # no workspace for no row
+    assert lib.csa_topk(None, None, 0, 10, 0, None, None, 0, None) == INVALID
+    assert lib.csa_topk(None, None, 2, 0, 4, None, None, 0, None) == INVALID    # rows to fill need idx
+    assert lib.csa_topk_noalloc(None, None, 0, 10, 4, None, None) == 0
+    anul = dict(q=None, cmp=None, idx=None, win=None, pos=None, sink=None, out=None, ws=None, ws_bytes=0)
+    assert _attn(lib, B=0, **anul) == 0
+    assert _attn(lib, S=0, **anul) == 0
+    assert _attn(lib, B=0, H=0, **anul) == INVALID
+    assert lib.hca_attn(None, None, 8192, 128, None, 128, 128, None, None, 1, 0.04, 64, 1e4, 0, 1, 64, 512, None,
+                        0, None, 0, None) == 0
+    assert lib.hca_attn(None, None, 8192, 0, None, 128, 128, None, None, 1, 0.04, 64, 1e4, 0, 1, 64, 512, None,
+                        0, None, 0, None) == INVALID
+    assert lib.csa_kv4_quantize(None, 1, 0, 512, 64, None, None) == 0
+    assert lib.csa_kv4_quantize(None, 1, 0, 500, 64, None, None) == INVALID
+    assert _qproj(lib, M=0, x=None, wq_a=None, gamma=None, wq_b=None, pos=None, q=None, ws=None, ws_bytes=0) == 0
+    assert _oproj(lib, M=0, o=None, wo_a=None, wo_b=None, y=None, ws=None, ws_bytes=0) == 0
+    assert _oproj(lib, M=0, o=None, wo_a=None, wo_b=None, y=None, ws=None, ws_bytes=0, o_dtype=3) == INVALID
+    # paged calls: an empty batch reads no page table, which may be absent
+    assert lib.csa_index_score_paged(None, None, None, 1, None, 0, 1, 64, 128, None, 4, None, None) == 0
+    assert lib.csa_index_score_paged(None, None, None, 1, None, 2, 1, 64, 128, None, 4, None, None) == INVALID
+    assert lib.csa_sparse_attn_paged(None, None, None, None, 512, None, 128, 128, None, None, 1, 0.04, 64, 1e4,
+                                     0, 1, 64, 512, None, 0, None, 0, None) == 0
+    assert lib.hca_attn_paged(None, None, None, 128, None, 128, 128, None, None, 1, 0.04, 64, 1e4, 0, 1, 64, 512,
+                              None, 0, None, 0, None) == 0
+    job = CompressJob(None, None, None, None, 1, None, 0, 16, 16 * 512, 512, 4, 1, 64, 1e4, 1e-6, 0, 0, 0, P, None,
+                      1, 0, 0, None, 0)
+    tab = PageTableC(None, 0, 0, 0)
+    assert lib.csa_compress_paged(ctypes.byref(job), ctypes.byref(tab), 1, None) == 0
+    job.B = 2
+    assert lib.csa_compress_paged(ctypes.byref(job), ctypes.byref(tab), 1, None) == INVALID

@@ -791,3 +791,55 @@ def test_tiny_config_end_to_end():
                                oracle.pipeline.window_rows(want["win"], t, W), inp["sink"], scale, t,
                                cfg.rope_dim, cfg.rope_base)
         assert_attn(outs[t], o, what=f"out t={t}", max_abs=1e-4, mean_abs=1e-5)
+
+
+# ---------------------------------------------------------------------------
+# Calls with no work
+# ---------------------------------------------------------------------------
+def test_calls_with_no_work():
+    """Empty batches through the binding (torch hands NULL for empty tensors):
+    every entry point returns without error and writes nothing; a span-mode
+    compressor call with no entry leaves its output alone, and top-k rows of
+    no position select nothing (-1)."""
+    csa = csa_mod()
+    bf, i32, c = torch.bfloat16, torch.int32, "cuda"
+    e = lambda *shape, dtype=torch.float32: torch.empty(shape, dtype=dtype, device=c)
+    gamma = torch.ones(512, device=c)
+    csa.csa_compress(e(0, 16, 512, dtype=bf), e(0, 16, 512, dtype=bf), gamma, e(0, 4, 512), ratio=4, overlap=1,
+                     rope_dim=64, pos=e(0, dtype=i32))
+    csa.csa_compress(e(0, 128, 512, dtype=bf), e(0, 128, 512, dtype=bf), gamma, e(0, 4, 512), ratio=128, overlap=0,
+                     rope_dim=64, pos=e(0, dtype=i32))
+    kv = dev_bf16(rows_bf16(1, (2, 16, 512)))
+    out = torch.full((2, 4, 512), 7.0, device=c)
+    csa.csa_compress(kv, kv.clone(), gamma, out, ratio=4, overlap=1, rope_dim=64, n_entries=0)
+    csa.csa_index_score(e(0, 1, 64, 128, dtype=bf), e(0, 1, 64), e(0, 1000, 128, dtype=bf), e(0, 1, dtype=i32),
+                        e(0, 1, 1000), ratio=4)
+    csa.csa_index_score(dev_bf16(rows_bf16(2, (2, 1, 64, 128))), torch.ones((2, 1, 64), device=c),
+                        e(2, 0, 128, dtype=bf), torch.zeros((2, 1), dtype=i32, device=c), e(2, 1, 0), ratio=4)
+    csa.csa_topk(e(0, 16384), None, 512, e(0, 512, dtype=i32))
+    csa.csa_topk_noalloc(e(0, 16384), None, 512, e(0, 512, dtype=i32))
+    idx = torch.full((3, 8), 5, dtype=i32, device=c)
+    csa.csa_topk(e(3, 0), None, 8, idx)
+    idx2 = torch.full((3, 8), 5, dtype=i32, device=c)
+    csa.csa_topk_noalloc(e(3, 0), None, 8, idx2)
+    q, cmp, win, pos, sink = e(0, 1, 64, 512, dtype=bf), e(0, 100, 512, dtype=bf), e(0, 128, 512, dtype=bf), \
+        e(0, 1, dtype=i32), torch.zeros(64, device=c)
+    csa.csa_sparse_attn(q, cmp, e(0, 1, 512, dtype=i32), win, pos, sink, e(0, 1, 64, 512), window=128,
+                        scale=0.04, rope_dim=64)
+    csa.hca_attn(q, cmp, win, pos, sink, e(0, 1, 64, 512), ratio=128, window=128, scale=0.04, rope_dim=64)
+    pages, pool = e(0, 4, dtype=i32), e(256, 512, dtype=bf)
+    csa.csa_sparse_attn_paged(q, pool, pages, e(0, 1, 512, dtype=i32), win, pos, sink, e(0, 1, 64, 512),
+                              page_rows=64, window=128, scale=0.04, rope_dim=64)
+    csa.hca_attn_paged(q, pool, pages, win, pos, sink, e(0, 1, 64, 512), page_rows=64, ratio=128, window=128,
+                       scale=0.04, rope_dim=64)
+    csa.csa_index_score_paged(e(0, 1, 64, 128, dtype=bf), e(0, 1, 64), e(256, 128, dtype=bf), e(0, 1, dtype=i32),
+                              e(0, 1, 256), pages, page_rows=64, ratio=4)
+    csa.csa_compress_paged(e(0, 16, 512, dtype=bf), e(0, 16, 512, dtype=bf), gamma, pool, pages, page_rows=64,
+                           ratio=4, overlap=1, rope_dim=64, pos=e(0, dtype=i32))
+    csa.csa_kv4_quantize(e(0, 512, dtype=bf), e(0, csa.csa_kv4_row_bytes(512, 64), dtype=torch.uint8), rope_dim=64)
+    csa.csa_q_proj(e(0, 256, dtype=bf), e(128, 256, dtype=bf), torch.ones(128, device=c), e(256, 128, dtype=bf),
+                   e(0, dtype=i32), e(0, 2, 128, dtype=bf), rope_dim=64)
+    csa.csa_out_proj(e(0, 2, 128, dtype=bf), e(2, 128, 128, dtype=bf), e(256, 256, dtype=bf), e(0, 256))
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+    assert bool((idx == -1).all()) and bool((idx2 == -1).all())
