@@ -53,6 +53,8 @@ def rows_bf16(seed, shape, unit=False):
     (512, 128, 0, 64, 384, 0, 0, 3),     # HCA ratio, no overlap
     (256, 2, 1, 32, 14, 0, 0, 7),        # other lane width
     (96, 4, 1, 16, 20, 0, 0, 5),         # general path (D not a lane multiple)
+    (2048, 4, 1, 64, 12, 0, 0, 3),       # widest lane-kernel row: 16 waves of channel pairs
+    (8192, 4, 1, 64, 12, 0, 0, 3),       # widest row accepted (general path)
 ])
 def test_compress_span(D, ratio, overlap, rope, T, tok0, e0, n):
     csa = csa_mod()
@@ -425,6 +427,8 @@ def test_index_score_long_cache_batches(B, S, Ncap, full):
     (3, 40000, 512, "ragged"), (2, 300000, 1024, None), (2, 700, 512, None), (64, 2048, 512, "causal"),
     # lengths that are not a multiple of four take the one-key loads
     (3, 101, 4, None), (2, 30001, 512, "ragged"), (2, 20000, 37, None),
+    # the largest k accepted: more than a row holds, one tile, and chunked rows
+    (2, 1500, 4096, None), (2, 6000, 4096, "ragged"), (2, 50000, 4096, None),
 ])
 def test_topk_exact(R, N, k, nvalid):
     csa = csa_mod()
