@@ -103,7 +103,7 @@ __global__ __launch_bounds__(THREADS) void topk_select(SelectArgs a) {
   __shared__ uint32_t wsum[W + 1];
   __shared__ uint32_t wcount[W];
   __shared__ float wlo[W], whi[W];
-  __shared__ uint32_t list[THREADS];  // keys of the threshold bin
+  __shared__ __attribute__((aligned(16))) uint32_t list[THREADS];  // keys of the threshold bin, then zeros
   __shared__ uint32_t nlist, sh_bin, sh_above, sh_thr, sh_need;
   __shared__ uint32_t pick[2];
 
@@ -114,6 +114,7 @@ __global__ __launch_bounds__(THREADS) void topk_select(SelectArgs a) {
   if (!FROM_CAND && a.n_valid != nullptr) len = min(len, max(a.n_valid[row], 0));
   for (int i = lane; i < 256; i += kWave) hist[wave][i] = 0;  // own wave's histogram
   if (tid == 0) nlist = 0;
+  list[tid] = 0u;  // a zero key is never larger than, nor equal to, a valid key
 
   // Coalesced, straight-line loads (position tid + t*THREADS, or four keys
   // at 4*(tid + j*THREADS) when rows are 16-byte aligned); the keys then
@@ -290,10 +291,13 @@ __global__ __launch_bounds__(THREADS) void topk_select(SelectArgs a) {
       if (tid < int(n)) {
         const uint32_t key = list[tid];
         uint32_t gt = 0, eqc = 0;
-        for (uint32_t j = 0; j < n; ++j) {
-          const uint32_t kj = list[j];
-          gt += kj > key;
-          eqc += kj == key;
+        // four keys per LDS read (the zeros past the list count for nothing)
+        const uint4* l4 = reinterpret_cast<const uint4*>(list);
+#pragma unroll 2
+        for (uint32_t j = 0; j < n; j += 4) {
+          const uint4 v = l4[j / 4];
+          gt += uint32_t(v.x > key) + uint32_t(v.y > key) + uint32_t(v.z > key) + uint32_t(v.w > key);
+          eqc += uint32_t(v.x == key) + uint32_t(v.y == key) + uint32_t(v.z == key) + uint32_t(v.w == key);
         }
         if (gt < remaining && remaining <= gt + eqc) { sh_thr = key; sh_need = remaining - gt; }
       }
