@@ -622,8 +622,11 @@ __global__ __launch_bounds__(kThreads) void attn_mfma(AttnArgs a, int nsplit, in
 
 // Merge the splits of one query with the sink, inverse RoPE, store.  grid
 // (B*S, 64): workgroup y = (v, dp, ht) takes partial block y of every split;
-// 256 threads, wave w sums the splits w, w+4, ... (all its loads in flight
-// at once), the four sums meet in LDS.
+// 256 threads, wave w sums the splits w, w+4, ... (BATCH of its loads in
+// flight at once), the four sums meet in LDS.  A small BATCH for few splits
+// keeps the registers low enough for eight workgroups per CU, so that large
+// batches of queries (64 workgroups each) merge in one round.
+template <int BATCH>
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int nsplit) {
   __shared__ __attribute__((aligned(16))) float part[4][kWave][8];
   // per split and head of the block: reference, sum, log2 of the stored scale
@@ -641,7 +644,7 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int nsplit) {
   const uint4* ws_o = static_cast<const uint4*>(a.ws) + qi * nsplit * kPartialVecs + blk * kWave + lane;
   // this wave's partials (splits wave, wave + 4, ...) are requested first:
   // they need no record, so their latency overlaps the records' own
-  constexpr int kBatch = kMaxSplits / 4 / 4;  // splits per wave held at once
+  constexpr int kBatch = BATCH;  // splits per wave held at once
   uint4 u[kBatch];
 #pragma unroll
   for (int j = 0; j < kBatch; ++j) {
@@ -1268,9 +1271,12 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, bool hca, hipStr
       else CSA_ATTN_MFMA(false, false, false);
     }
 #undef CSA_ATTN_MFMA
-    if (plan.nsplit > 1)
-      hipLaunchKernelGGL(attn_combine, dim3(unsigned(nq), kPartialVecs / kWave), dim3(256),
-                         size_t(3) * plan.nsplit * 16 * sizeof(float), stream, a, plan.nsplit);
+    if (plan.nsplit > 1) {
+      const dim3 grid(unsigned(nq), kPartialVecs / kWave);
+      const size_t rec = size_t(3) * plan.nsplit * 16 * sizeof(float);
+      if (plan.nsplit <= 16) hipLaunchKernelGGL((attn_combine<4>), grid, dim3(256), rec, stream, a, plan.nsplit);
+      else hipLaunchKernelGGL((attn_combine<kMaxSplits / 16>), grid, dim3(256), rec, stream, a, plan.nsplit);
+    }
   } else {
     const dim3 grid(unsigned(nq), a.H);
     if (hca) hipLaunchKernelGGL((attn_any<true>), grid, dim3(kWave), a.D * sizeof(float), stream, a);
