@@ -526,10 +526,12 @@ def test_hca_attn_mfma():
     assert_attn(host(out), want, what="hca")
 
 
-@pytest.mark.parametrize("case", ["csa8", "hca4", "csa100"])
+@pytest.mark.parametrize("case", ["csa8", "hca4", "csa100", "csa16", "csa17"])
 def test_split_decode_shapes(case):
     """The split decode path at the bench's split counts (CSA: 8 queries in
-    10 splits; HCA: 4 queries in 52) and at 100 queries in 3 splits: each
+    10 splits; HCA: 4 queries in 52), at 100 queries in 3 splits, and at 16
+    and 17 splits (the largest split count whose combine holds four partial
+    loads per wave, and the smallest that takes the wide batch): each
     matches the oracle, and three calls on one workspace give the same
     bits."""
     csa = csa_mod()
@@ -543,6 +545,11 @@ def test_split_decode_shapes(case):
         B, Ncap, k, r = 8, 16384, 512, 4
         pos = np.array([[4 * Ncap - 1], [4 * 9000 + 3], [130], [5000], [4 * Ncap - 2], [600], [127], [4 * 12345]],
                        np.int32)
+        only = None
+    elif case in ("csa16", "csa17"):
+        # window + k = 1024 or 1088 candidates over 64-row splits
+        B, Ncap, k, r = 2, 2048, (896 if case == "csa16" else 960), 4
+        pos = np.array([[4 * Ncap - 1], [4 * 1500 + 2]], np.int32)
         only = None
     else:
         B, Ncap, k, r = 100, 2048, 512, 4
